@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark: forward + backward of the 2D Gaussian splatting layer on one GPU.
+
+One step = forward (per-Gaussian preprocessing, tile binning, forward raster)
+plus backward (gradient raster reusing the forward's binning, finalisation)
+over one batch: 384 frames of 128x128x3 with 4096 Gaussians each (32 x 12
+frames, scales log-uniform in [0.5, 8] px, anisotropy up to 4:1, amplitudes
+N(0, 0.5), 3-sigma truncation), seeded synthetic inputs resident in HBM.
+
+Prints one JSON line.  ``value`` is Gaussian-pixel evaluations per second for
+forward + backward: the number of (Gaussian, pixel) pairs inside the
+truncation, counted exactly by the CPU oracle, divided by the step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector: 256 CU x 2.4 GHz x 256 flop/clk
+HBM_PEAK_GBS = 8000.0
+
+
+def flops_per_pair(C):
+    """Algorithmic flops per support pair (add/mul = 1, fma = 2, exp = 1,
+    compare/select = 0): forward d(2) z(6) q(3) exp(1) accumulate(2C);
+    backward recompute(12) h(2C-1) v(1) A(2C) five sums(10)."""
+    return 12 + 2 * C, 24 + 4 * C
+
+
+def kernel_bytes(B, N, H, W, C, pairs_tiles):
+    """Algorithmic HBM bytes per launch of each kernel (each tensor moved once)."""
+    BN, img = B * N, B * H * W * C * 4
+    nT = ((H + 15) // 16) * ((W + 15) // 16)
+    P = 5 + C
+    return {
+        "preprocess": BN * P * 4 + BN * 40,
+        "bin_count": BN * 8 + B * nT * 4,
+        "scan": 2 * B * nT * 4,
+        "bin_write": BN * 8 + B * nT * 4 + pairs_tiles * 4,
+        "forward_raster": pairs_tiles * 4 + BN * (32 + C * 4) + img,
+        "zero_verify": BN * P * 4,
+        "backward_raster": pairs_tiles * 4 + BN * (32 + C * 4) + img + 2 * BN * P * 4,
+        "finalize": 2 * BN * P * 4 + BN * P * 4,
+    }
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline_leg(params, grad, wl, radius, budget_s, want_count=True):
+    """The oracle (fp64 CPU) timed on this host's cores on a bounded sample of
+    the workload's frames; also counts the support pairs of the full batch."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.default_threads()
+    total_pairs = None
+    if want_count:
+        total_pairs = int(oracle.count_support(params, wl.H, wl.W, radius, nthreads=threads).sum())
+    # size the sample from a 4-frame probe so the timed run is ~budget_s
+    probe = min(4, wl.B)
+    t0 = time.perf_counter()
+    oracle.render(params[:probe], wl.H, wl.W, radius, extras=False, nthreads=threads)
+    oracle.grad(params[:probe], grad[:probe], wl.H, wl.W, radius, extras=False, nthreads=threads)
+    per_frame = (time.perf_counter() - t0) / probe * min(probe, threads)
+    frames = int(max(1, min(wl.B, budget_s * threads / max(per_frame, 1e-6))))
+    frames = max(1, (frames // threads) * threads) if frames >= threads else frames
+    sp, sg = params[:frames], grad[:frames]
+    t0 = time.perf_counter()
+    _, _, _, pairs = oracle.render(sp, wl.H, wl.W, radius, extras=False, nthreads=threads)
+    oracle.grad(sp, sg, wl.H, wl.W, radius, extras=False, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": float(pairs.sum()) / dt,
+        "unit": "evals/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d frames, forward+backward, fp64 C, %.2f s wall" % (frames, wl.B, dt),
+        "frames_per_s": frames / dt,
+    }, total_pairs
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--radius", type=float, default=3.0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="target wall seconds of the oracle baseline run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-loop", type=int, default=0,
+                    help="only run this many steps (for rocprofv3), print nothing else")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(frames are independent; see the design notes on sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import _lib, workloads
+
+    wl, params_np, grad_np = workloads.make_inputs(args.workload)
+    B, N, H, W, C = wl.B, wl.N, wl.H, wl.W, wl.C
+    dev = torch.device("cuda:0")
+    params = torch.from_numpy(params_np).to(dev)
+    grad_image = torch.from_numpy(grad_np).to(dev)
+    image = torch.empty((B, H, W, C), dtype=torch.float32, device=dev)
+    grad_params = torch.empty_like(params)
+    st = torch.cuda.current_stream(dev).cuda_stream
+
+    # exact list capacity from one binning pass
+    ws_fixed = _lib.pdr_splat_workspace_bytes(B, N, H, W, C, 0)
+    nT = ((H + 15) // 16) * ((W + 15) // 16)
+    probe = torch.empty(ws_fixed, dtype=torch.uint8, device=dev)
+    off = torch.empty(B * nT + 1, dtype=torch.int32, device=dev)
+    lst = torch.empty(1, dtype=torch.int32, device=dev)
+    _lib.pdr_splat_bin(params.data_ptr(), B, N, H, W, C, args.radius, off.data_ptr(),
+                       lst.data_ptr(), 0, probe.data_ptr(), ws_fixed, st)
+    _, tile_pairs = _lib.pdr_splat_check(probe.data_ptr(), st)
+    del probe, off, lst
+    ws_bytes = _lib.pdr_splat_workspace_bytes(B, N, H, W, C, tile_pairs)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step():
+        _lib.pdr_splat_forward(params.data_ptr(), image.data_ptr(), B, N, H, W, C, args.radius,
+                               ws.data_ptr(), ws_bytes, st)
+        _lib.pdr_splat_backward(params.data_ptr(), grad_image.data_ptr(), grad_params.data_ptr(),
+                                B, N, H, W, C, args.radius, ws.data_ptr(), ws_bytes, 1, st)
+
+    step()
+    rc, _ = _lib.pdr_splat_check(ws.data_ptr(), st)
+    if rc != 0:
+        raise SystemExit("first step failed: %s" % _lib.status_string(rc))
+
+    if args.profile_loop:
+        for _ in range(args.profile_loop):
+            step()
+        torch.cuda.synchronize()
+        print("profile loop done: %d steps" % args.profile_loop, flush=True)
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events on the launch stream and a host clock
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - h0) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations: the same K steps with HIP events around every launch
+    _lib.pdr_splat_timing(True)
+    _lib.pdr_splat_timing_read(reset=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_events = e0.elapsed_time(e1) / args.steps
+    per_kernel = _lib.pdr_splat_timing_read(reset=True)
+    _lib.pdr_splat_timing(False)
+    rc, _ = _lib.pdr_splat_check(ws.data_ptr(), st)
+    if rc != 0:
+        raise SystemExit("timed steps failed: %s" % _lib.status_string(rc))
+
+    cpu, support_pairs = None, None
+    if not args.no_cpu_baseline:
+        cpu, support_pairs = cpu_baseline_leg(params_np, grad_np, wl, args.radius, args.cpu_budget)
+
+    f_fwd, f_bwd = flops_per_pair(C)
+    kernels = {}
+    kb = kernel_bytes(B, N, H, W, C, tile_pairs)
+    for name, (tot_ms, cnt) in per_kernel.items():
+        if cnt == 0:
+            continue
+        avg = tot_ms / cnt
+        row = {"avg_ms": round(avg, 5), "launches_per_step": cnt // args.steps,
+               "alg_GBps": round(kb[name] / (avg * 1e-3) / 1e9, 1)}
+        if support_pairs is not None and name in ("forward_raster", "backward_raster"):
+            fl = support_pairs * (f_fwd if name == "forward_raster" else f_bwd)
+            row["alg_TFLOPs"] = round(fl / (avg * 1e-3) / 1e12, 3)
+        kernels[name] = row
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    roofline = None
+    if support_pairs is not None:
+        fl = support_pairs * (f_fwd if dom == "forward_raster" else f_bwd)
+        avg = kernels[dom]["avg_ms"] * 1e-3
+        ach = fl / avg / 1e12
+        traffic = None
+        tpath = os.path.join(ROOT, "profiles", "traffic_%s_cfg%d.json" % (dom, args.workload))
+        if os.path.exists(tpath):
+            with open(tpath) as fh:
+                t = json.load(fh)
+            if t.get("source_digest") == source_digest(t.get("sources", [])):
+                traffic = t.get("bytes_per_launch")
+        roofline = {"bound": "alu", "achieved": round(ach, 3), "peak": FP32_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / FP32_PEAK_TFLOPS, 4),
+                    "traffic": traffic, "kernel": dom,
+                    "flops_per_launch": fl, "avg_launch_ms": kernels[dom]["avg_ms"]}
+    value = support_pairs / (ms * 1e-3) if support_pairs is not None else None
+    out = {
+        "metric": "fwd+bwd Gaussian-pixel evals/s and frames/s at 128x128x3, N=4096; % FP32 peak",
+        "value": value,
+        "unit": "evals/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "%d frames of %dx%dx%d, N=%d Gaussians/frame, 3-sigma truncation"
+                   % (B, H, W, C, N), "frames": B, "H": H, "W": W, "C": C,
+                   "gaussians_per_frame": N, "radius": args.radius},
+        "frames_per_s": B / (ms * 1e-3),
+        "support_pairs": support_pairs,
+        "tile_pairs": int(tile_pairs),
+        "fp32_peak_frac_fwd_bwd": (round(support_pairs * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
+                                         / FP32_PEAK_TFLOPS, 4) if support_pairs else None),
+        "ms_per_step_host": round(host_ms, 5),
+        "ms_per_step_with_kernel_events": round(ms_events, 5),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

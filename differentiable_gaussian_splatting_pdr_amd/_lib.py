@@ -1,0 +1,139 @@
+"""ctypes binding of ``libpdrsplat.so`` (the C ABI in ``include/pdr_splat.h``).
+
+Argument marshalling only: every function here forwards to the entry point of
+the same name and turns a negative status into :class:`PdrError`.  Pointers
+are passed as integers (device addresses, ``hipStream_t`` handles).  There is
+no fallback: if the library is not built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpdrsplat.so")
+
+PDR_OK = 0
+PDR_ERR_INVALID_ARG = -1
+PDR_ERR_WORKSPACE = -2
+PDR_ERR_HIP = -3
+PDR_ERR_OVERFLOW = -4
+PDR_ERR_STALE = -5
+
+EXPORTED = (
+    "pdr_splat_tile_size",
+    "pdr_splat_workspace_bytes",
+    "pdr_splat_forward",
+    "pdr_splat_backward",
+    "pdr_splat_bin",
+    "pdr_splat_check",
+    "pdr_splat_status_string",
+    "pdr_splat_timing",
+    "pdr_splat_timing_read",
+    "pdr_splat_kernel_name",
+)
+
+KERNEL_COUNT = 8
+
+
+class PdrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (where, status_string(status), status))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libpdrsplat.so is not built (expected at %s); run "
+                "`python -m differentiable_gaussian_splatting_pdr_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        i, ll, f, vp, sz = ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+        L.pdr_splat_tile_size.argtypes = []
+        L.pdr_splat_tile_size.restype = i
+        L.pdr_splat_workspace_bytes.argtypes = [i, i, i, i, i, ll]
+        L.pdr_splat_workspace_bytes.restype = ll
+        L.pdr_splat_forward.argtypes = [vp, vp, i, i, i, i, i, f, vp, sz, vp]
+        L.pdr_splat_forward.restype = i
+        L.pdr_splat_backward.argtypes = [vp, vp, vp, i, i, i, i, i, f, vp, sz, i, vp]
+        L.pdr_splat_backward.restype = i
+        L.pdr_splat_bin.argtypes = [vp, i, i, i, i, i, f, vp, vp, ll, vp, sz, vp]
+        L.pdr_splat_bin.restype = i
+        L.pdr_splat_check.argtypes = [vp, vp, ctypes.POINTER(ll)]
+        L.pdr_splat_check.restype = i
+        L.pdr_splat_status_string.argtypes = [i]
+        L.pdr_splat_status_string.restype = ctypes.c_char_p
+        L.pdr_splat_timing.argtypes = [i]
+        L.pdr_splat_timing.restype = i
+        L.pdr_splat_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ll), i]
+        L.pdr_splat_timing_read.restype = i
+        L.pdr_splat_kernel_name.argtypes = [i]
+        L.pdr_splat_kernel_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _raise(rc: int, where: str) -> int:
+    if rc < 0:
+        raise PdrError(rc, where)
+    return rc
+
+
+def status_string(status: int) -> str:
+    return lib().pdr_splat_status_string(int(status)).decode()
+
+
+def pdr_splat_tile_size() -> int:
+    return lib().pdr_splat_tile_size()
+
+
+def pdr_splat_workspace_bytes(B, N, H, W, C, max_pairs) -> int:
+    return _raise(lib().pdr_splat_workspace_bytes(B, N, H, W, C, int(max_pairs)),
+                  "pdr_splat_workspace_bytes")
+
+
+def pdr_splat_forward(params, image, B, N, H, W, C, radius, workspace, workspace_bytes, stream):
+    return _raise(lib().pdr_splat_forward(params, image, B, N, H, W, C, float(radius), workspace,
+                                          workspace_bytes, stream), "pdr_splat_forward")
+
+
+def pdr_splat_backward(params, grad_image, grad_params, B, N, H, W, C, radius, workspace,
+                       workspace_bytes, reuse_binning, stream):
+    return _raise(lib().pdr_splat_backward(params, grad_image, grad_params, B, N, H, W, C,
+                                           float(radius), workspace, workspace_bytes,
+                                           int(reuse_binning), stream), "pdr_splat_backward")
+
+
+def pdr_splat_bin(params, B, N, H, W, C, radius, tile_off, tile_list, cap, workspace,
+                  workspace_bytes, stream):
+    return _raise(lib().pdr_splat_bin(params, B, N, H, W, C, float(radius), tile_off, tile_list,
+                                      int(cap), workspace, workspace_bytes, stream),
+                  "pdr_splat_bin")
+
+
+def pdr_splat_check(workspace, stream):
+    """Return (status, pairs_needed); the status is not raised."""
+    n = ctypes.c_longlong(0)
+    rc = lib().pdr_splat_check(workspace, stream, ctypes.byref(n))
+    return rc, n.value
+
+
+def pdr_splat_timing(enable: bool) -> bool:
+    return bool(lib().pdr_splat_timing(int(bool(enable))))
+
+
+def pdr_splat_kernel_name(kid: int) -> str:
+    return lib().pdr_splat_kernel_name(int(kid)).decode()
+
+
+def pdr_splat_timing_read(reset: bool = True):
+    """Return {kernel name: (total_ms, launches)} accumulated since the last reset."""
+    ms = (ctypes.c_double * KERNEL_COUNT)()
+    cnt = (ctypes.c_longlong * KERNEL_COUNT)()
+    _raise(lib().pdr_splat_timing_read(ms, cnt, int(bool(reset))), "pdr_splat_timing_read")
+    return {pdr_splat_kernel_name(k): (ms[k], cnt[k]) for k in range(KERNEL_COUNT)}

@@ -1,0 +1,148 @@
+// abi.hip -- the extern "C" entry points declared in include/pdr_splat.h:
+// argument validation, workspace carve-up and kernel launches on the
+// caller's stream.  No allocation happens here.
+#include <math.h>
+#include <stdint.h>
+
+#include "pdr_common.hpp"
+#include "pdr_internal.hpp"
+#include "pdr_splat.h"
+
+using namespace pdr;
+
+namespace {
+
+struct Dims {
+  long long BN, BT;
+  int nTx, nTy;
+};
+
+int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
+  if (B < 1 || N < 1 || H < 1 || W < 1 || C < 1) return PDR_ERR_INVALID_ARG;
+  if (H > kMaxHW || W > kMaxHW || N > kMaxN) return PDR_ERR_INVALID_ARG;
+  long long BN = (long long)B * N;
+  if (BN > 0x7fffffffLL || BN * (5 + C) > 0x7fffffffffffLL) return PDR_ERR_INVALID_ARG;
+  if ((long long)B * H * W * C > (1LL << 46)) return PDR_ERR_INVALID_ARG;
+  d->nTx = (W + kTile - 1) / kTile;
+  d->nTy = (H + kTile - 1) / kTile;
+  d->BN = BN;
+  d->BT = (long long)B * d->nTx * d->nTy;
+  if (d->BT + 1 > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
+  return PDR_OK;
+}
+
+int validate_radius(float radius) {
+  return (isfinite(radius) && radius > 0.f) ? PDR_OK : PDR_ERR_INVALID_ARG;
+}
+
+// The workspace layout implied by its size: the fixed part, then as many
+// list entries as fit.
+int layout_for(const Dims &d, void *ws, size_t bytes, Layout *L) {
+  if (!ws) return PDR_ERR_INVALID_ARG;
+  if (((uintptr_t)ws & 255u) != 0) return PDR_ERR_WORKSPACE;
+  Layout fixed = make_layout(d.BN, d.BT, 0);
+  if (bytes < fixed.list) return PDR_ERR_WORKSPACE;
+  long long cap = (long long)((bytes - fixed.list) / 4);
+  if (cap > 0x7fffffffLL) cap = 0x7fffffffLL;
+  *L = make_layout(d.BN, d.BT, cap);
+  L->total = bytes;
+  return PDR_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PDR_OK : PDR_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int pdr_splat_tile_size(void) { return kTile; }
+
+long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long max_pairs) {
+  Dims d;
+  int rc = validate_sizes(B, N, H, W, C, &d);
+  if (rc != PDR_OK) return rc;
+  if (max_pairs < 0 || max_pairs > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
+  return (long long)make_layout(d.BN, d.BT, max_pairs).total;
+}
+
+int pdr_splat_forward(const float *params, float *image, int B, int N, int H, int W, int C,
+                      float radius, void *workspace, size_t workspace_bytes, void *stream) {
+  Dims d;
+  Layout L;
+  if (!params || !image) return PDR_ERR_INVALID_ARG;
+  int rc = validate_sizes(B, N, H, W, C, &d);
+  if (rc == PDR_OK) rc = validate_radius(radius);
+  if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
+  if (rc != PDR_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char *w = (char *)workspace;
+  hipError_t e = launch_binning(params, B, N, H, W, C, radius, workspace, L, (int *)(w + L.tile_off),
+                                (int *)(w + L.list), L.cap, true, st);
+  if (e == hipSuccess) e = launch_forward_raster(params, image, B, N, H, W, C, radius, workspace, L, st);
+  return hip_status(e);
+}
+
+int pdr_splat_backward(const float *params, const float *grad_image, float *grad_params, int B,
+                       int N, int H, int W, int C, float radius, void *workspace,
+                       size_t workspace_bytes, int reuse_binning, void *stream) {
+  Dims d;
+  Layout L;
+  if (!params || !grad_image || !grad_params) return PDR_ERR_INVALID_ARG;
+  int rc = validate_sizes(B, N, H, W, C, &d);
+  if (rc == PDR_OK) rc = validate_radius(radius);
+  if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
+  if (rc != PDR_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char *w = (char *)workspace;
+  hipError_t e = hipSuccess;
+  if (!reuse_binning)
+    e = launch_binning(params, B, N, H, W, C, radius, workspace, L, (int *)(w + L.tile_off),
+                       (int *)(w + L.list), L.cap, true, st);
+  if (e == hipSuccess)
+    e = launch_backward(params, grad_image, grad_params, B, N, H, W, C, radius, workspace, L,
+                        reuse_binning != 0, st);
+  return hip_status(e);
+}
+
+int pdr_splat_bin(const float *params, int B, int N, int H, int W, int C, float radius,
+                  int *tile_off, int *tile_list, long long cap, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  Dims d;
+  Layout L;
+  if (!params || !tile_off || !tile_list || cap < 0) return PDR_ERR_INVALID_ARG;
+  int rc = validate_sizes(B, N, H, W, C, &d);
+  if (rc == PDR_OK) rc = validate_radius(radius);
+  if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
+  if (rc != PDR_OK) return rc;
+  if (cap > 0x7fffffffLL) cap = 0x7fffffffLL;
+  // the workspace's own lists are not written: the stamp is left invalid so
+  // that a later backward reusing this workspace reports PDR_ERR_STALE
+  hipError_t e = launch_binning(params, B, N, H, W, C, radius, workspace, L, tile_off, tile_list,
+                                cap, false, (hipStream_t)stream);
+  return hip_status(e);
+}
+
+int pdr_splat_check(void *workspace, void *stream, long long *pairs_needed) {
+  if (!workspace) return PDR_ERR_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return PDR_ERR_HIP;
+  WsHeader h;
+  if (hipMemcpy(&h, workspace, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return PDR_ERR_HIP;
+  if (pairs_needed) *pairs_needed = h.total;
+  if (h.status & kStatusOverflow) return PDR_ERR_OVERFLOW;
+  if (h.status & kStatusStale) return PDR_ERR_STALE;
+  return PDR_OK;
+}
+
+const char *pdr_splat_status_string(int status) {
+  switch (status) {
+    case PDR_OK: return "ok";
+    case PDR_ERR_INVALID_ARG: return "invalid argument";
+    case PDR_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case PDR_ERR_HIP: return "HIP runtime or launch error";
+    case PDR_ERR_OVERFLOW: return "tile list capacity exceeded";
+    case PDR_ERR_STALE: return "workspace does not hold the binning of these arguments";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// pdr_common.hpp -- shared device/host definitions of the gfx950 splatting
+// library: workspace layout, per-Gaussian record, wave64 cross-lane helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pdr {
+
+constexpr int kTile = 16;        // tile edge in pixels (binning and raster)
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kBinThreads = 256; // binning workgroup
+constexpr int kScanThreads = 1024;
+constexpr int kMaxHW = 32767;    // pixel boxes are packed as 16-bit coordinates
+constexpr int kMaxN = 1 << 22;   // per-frame Gaussian count bound of the scan's int32 partials
+
+// sqrt(log2(e) / 2): whitening rows are scaled by it so that
+// exp(-q/2) == exp2(-(z1'^2 + z2'^2)) with z' = kappa * z.
+constexpr double kKappa = 0.84932180028801904272150283410289;
+constexpr double kKappa2 = 0.72134752044448170367996234050095;  // log2(e) / 2
+
+// Status bits raised on the device into the workspace header.
+constexpr int kStatusOverflow = 1;
+constexpr int kStatusStale = 2;
+
+struct WsHeader {
+  int status;        // kStatus* bits of the last call
+  int pad0;
+  long long total;   // (tile, Gaussian) pairs of the last binning
+  long long cap;     // list capacity used by the last binning
+  int stamp[8];      // B, N, H, W, C, radius bits, params pointer lo/hi at binning
+  int pad1[50];
+};
+static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
+
+// Per-Gaussian raster record (32 bytes, two 16-byte loads): mean, the
+// whitening rows scaled by kappa, and the packed pixel bounding box.
+struct __attribute__((aligned(16))) GRec {
+  float mx, my;
+  float l11, l12, l21, l22;
+  unsigned int bx;  // x0 | x1 << 16, inclusive; x0 > x1 means empty
+  unsigned int by;  // y0 | y1 << 16
+};
+static_assert(sizeof(GRec) == 32, "record is 32 bytes");
+
+constexpr unsigned int kEmptyBox = 0x0000FFFFu;  // x0 = 65535 > x1 = 0
+
+// Workspace carve-up; every region starts on a 256-byte boundary.
+struct Layout {
+  size_t hdr, recs, boxes, counts, tile_off, list, total;
+  long long cap;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline Layout make_layout(long long BN, long long BT, long long cap) {
+  Layout L;
+  size_t o = 0;
+  L.hdr = o;       o += align256(sizeof(WsHeader));
+  L.recs = o;      o += align256(size_t(BN) * sizeof(GRec));
+  L.boxes = o;     o += align256(size_t(BN) * 8);
+  L.counts = o;    o += align256(size_t(BT) * 4);
+  L.tile_off = o;  o += align256(size_t(BT + 1) * 4);
+  L.list = o;      o += align256(size_t(cap) * 4);
+  L.total = o;
+  L.cap = cap;
+  return L;
+}
+
+// ----------------------------------------------------------------------------
+// wave64 cross-lane helpers (DPP / ds_swizzle / permlane swaps)
+
+// DPP control words (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowRor8 = 0x128;  // within a 16-lane row: lane i <- lane i ^ 8
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Inclusive prefix sum of an int over the 64 lanes of a wave: row_shr steps
+// inside each 16-lane row, then row_bcast:15 / row_bcast:31 carry the row
+// totals into the rows above.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
+  return v;
+}
+
+__device__ __forceinline__ int wave_read(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// Value of the partner lane (lane ^ MASK), MASK in {1, 2, 4, 8, 16}.
+template <int MASK>
+__device__ __forceinline__ float xor_partner(float v) {
+  int x = __float_as_int(v);
+  if constexpr (MASK == 1) {
+    x = __builtin_amdgcn_update_dpp(0, x, kDppQuadXor1, 0xF, 0xF, false);
+  } else if constexpr (MASK == 2) {
+    x = __builtin_amdgcn_update_dpp(0, x, kDppQuadXor2, 0xF, 0xF, false);
+  } else if constexpr (MASK == 8) {
+    x = __builtin_amdgcn_update_dpp(0, x, kDppRowRor8, 0xF, 0xF, false);
+  } else {
+    static_assert(MASK == 4 || MASK == 16, "xor_partner mask");
+    // ds_swizzle bitmask mode: and 0x1f, or 0, xor MASK (within 32 lanes)
+    x = __builtin_amdgcn_ds_swizzle(x, 0x1F | (MASK << 10));
+  }
+  return __int_as_float(x);
+}
+
+// Sum with the partner lane for MASK in {4, 8, 16, 32} (an all-reduce step).
+template <int MASK>
+__device__ __forceinline__ float xor_sum(float v) {
+  if constexpr (MASK == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+  } else if constexpr (MASK == 32) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+  } else {
+    return v + xor_partner<MASK>(v);
+  }
+}
+
+// Blocks of a frame-major grid of (frame, item) are spread so that all items
+// of one frame go to the same XCD (workgroups are dealt to the 8 XCDs round
+// robin), keeping a frame's Gaussian records in one L2.
+__device__ __forceinline__ bool xcd_frame_item(int bid, int items, int frames, int *frame, int *item) {
+  int xcd = bid & 7;
+  int local = bid >> 3;
+  *frame = xcd + 8 * (local / items);
+  *item = local % items;
+  return *frame < frames;
+}
+
+inline long long xcd_grid(int items, int frames) { return 8LL * ((frames + 7) / 8) * items; }
+
+}  // namespace pdr

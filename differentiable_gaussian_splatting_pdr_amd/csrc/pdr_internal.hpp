@@ -1,0 +1,42 @@
+// pdr_internal.hpp -- host-side launchers shared by the C-ABI translation unit.
+#pragma once
+
+#include "pdr_common.hpp"
+#include "pdr_splat.h"
+
+namespace pdr {
+
+// Per-kernel event timing (no-ops unless pdr_splat_timing(1)).
+void timing_begin(int kid, hipStream_t st);
+void timing_end(int kid, hipStream_t st);
+
+#define PDR_TIMED(kid, st, launch) \
+  do {                             \
+    ::pdr::timing_begin(kid, st);  \
+    launch;                        \
+    ::pdr::timing_end(kid, st);    \
+  } while (0)
+
+constexpr int kMaxGroupTiles = 1024;    // tiles of one binning group (static LDS bases)
+constexpr long long kMaxChunk = 16384;  // Gaussians per binning chunk (bit-matrix columns)
+constexpr long long kBinLdsBytes = 60 * 1024;  // + 4 KB of static bases stays within 64 KB
+
+// K1 + count + scan + list write; tile_off/list may be the workspace's own
+// regions or caller buffers (inspection entry point, stamp_valid = false so
+// that the workspace does not claim to hold these lists).
+hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C, float radius,
+                          void *ws, const Layout &L, int *tile_off, int *list, long long cap,
+                          bool stamp_valid, hipStream_t st);
+
+// Forward raster: image[b][y][x][c] for all channels.
+hipError_t launch_forward_raster(const float *params, float *image, int B, int N, int H, int W,
+                                 int C, float radius, void *ws, const Layout &L, hipStream_t st);
+
+// Backward: zero grad_params (and verify the binning stamp when reusing),
+// raster the per-Gaussian sums with one atomic per wave per Gaussian, then
+// turn the sums into gradients in place.
+hipError_t launch_backward(const float *params, const float *grad_image, float *grad_params, int B,
+                           int N, int H, int W, int C, float radius, void *ws, const Layout &L,
+                           bool check_stamp, hipStream_t st);
+
+}  // namespace pdr

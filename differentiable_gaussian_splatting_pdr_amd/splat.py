@@ -1,0 +1,166 @@
+"""PyTorch-facing wrapper of the HIP splatting library.
+
+PyTorch provides device memory and the current HIP stream; all computation
+runs in the library's kernels through :mod:`._lib`.  Tensors must live on a
+ROCm device, be float32 and contiguous:
+
+  params       [B, N, 5 + C]  (mu_x, mu_y, s1, s2, theta, a_0 .. a_{C-1})
+  image        [B, H, W, C]
+  grad_params  [B, N, 5 + C]
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_params(params: torch.Tensor):
+    if not isinstance(params, torch.Tensor) or params.device.type != "cuda":
+        raise ValueError("params must be a tensor on a ROCm device")
+    if params.dtype != torch.float32 or params.dim() != 3 or params.shape[2] < 6:
+        raise ValueError("params must be float32 [B, N, 5 + C] with C >= 1")
+    if not params.is_contiguous():
+        raise ValueError("params must be contiguous")
+    B, N, P = params.shape
+    return B, N, P - 5
+
+
+class Workspace:
+    """Caller-owned device workspace (binning records, tile lists)."""
+
+    def __init__(self, device, nbytes: int = 0):
+        self.device = torch.device(device)
+        self.buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+    def ensure(self, nbytes: int):
+        if nbytes > self.nbytes:
+            self.buf = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device)
+        return self
+
+    @staticmethod
+    def bytes_for(B, N, H, W, C, max_pairs) -> int:
+        return _lib.pdr_splat_workspace_bytes(B, N, H, W, C, max_pairs)
+
+
+def _initial_pairs(B, N, H, W) -> int:
+    # a few tiles per Gaussian; grown exactly on overflow
+    t = _lib.pdr_splat_tile_size()
+    ntiles = ((H + t - 1) // t) * ((W + t - 1) // t)
+    return min(B * N * min(8, ntiles), 0x7FFFFFFF)
+
+
+def forward(params: torch.Tensor, H: int, W: int, radius: float = 3.0,
+            workspace: Workspace | None = None, image: torch.Tensor | None = None):
+    """Render; returns (image, workspace).  Synchronises once to check the
+    list capacity and re-runs with an exactly sized workspace on overflow."""
+    B, N, C = _check_params(params)
+    dev = params.device
+    ws = workspace or Workspace(dev)
+    ws.ensure(Workspace.bytes_for(B, N, H, W, C, _initial_pairs(B, N, H, W)))
+    if image is None:
+        image = torch.empty((B, H, W, C), dtype=torch.float32, device=dev)
+    st = _stream(dev)
+    for _ in range(2):
+        _lib.pdr_splat_forward(params.data_ptr(), image.data_ptr(), B, N, H, W, C, radius,
+                               ws.ptr, ws.nbytes, st)
+        rc, need = _lib.pdr_splat_check(ws.ptr, st)
+        if rc == _lib.PDR_OK:
+            return image, ws
+        if rc != _lib.PDR_ERR_OVERFLOW:
+            raise _lib.PdrError(rc, "pdr_splat_forward")
+        ws.ensure(Workspace.bytes_for(B, N, H, W, C, need))
+    raise _lib.PdrError(_lib.PDR_ERR_OVERFLOW, "pdr_splat_forward")
+
+
+def backward(params: torch.Tensor, grad_image: torch.Tensor, H: int, W: int,
+             radius: float = 3.0, workspace: Workspace | None = None,
+             reuse_binning: bool = False, grad_params: torch.Tensor | None = None,
+             check: bool = True):
+    """dL/dparams for dL/dimage; returns grad_params."""
+    B, N, C = _check_params(params)
+    dev = params.device
+    if grad_image.shape != (B, H, W, C) or grad_image.dtype != torch.float32:
+        raise ValueError("grad_image must be float32 [B, H, W, C]")
+    grad_image = grad_image.contiguous()
+    if grad_params is None:
+        grad_params = torch.empty_like(params)
+    st = _stream(dev)
+    if workspace is None:
+        reuse_binning = False
+        workspace = Workspace(dev, Workspace.bytes_for(B, N, H, W, C, _initial_pairs(B, N, H, W)))
+    for _ in range(2):
+        _lib.pdr_splat_backward(params.data_ptr(), grad_image.data_ptr(), grad_params.data_ptr(),
+                                B, N, H, W, C, radius, workspace.ptr, workspace.nbytes,
+                                int(reuse_binning), st)
+        if not check:
+            return grad_params
+        rc, need = _lib.pdr_splat_check(workspace.ptr, st)
+        if rc == _lib.PDR_OK:
+            return grad_params
+        if rc not in (_lib.PDR_ERR_OVERFLOW, _lib.PDR_ERR_STALE):
+            raise _lib.PdrError(rc, "pdr_splat_backward")
+        if rc == _lib.PDR_ERR_OVERFLOW:
+            workspace.ensure(Workspace.bytes_for(B, N, H, W, C, need))
+        reuse_binning = False
+    raise _lib.PdrError(rc, "pdr_splat_backward")
+
+
+def bin_lists(params: torch.Tensor, H: int, W: int, radius: float = 3.0):
+    """Binning only: returns (tile_off int32 [B*nT+1], tile_list int32 [pairs])."""
+    B, N, C = _check_params(params)
+    dev = params.device
+    t = _lib.pdr_splat_tile_size()
+    nT = ((H + t - 1) // t) * ((W + t - 1) // t)
+    ws = Workspace(dev, Workspace.bytes_for(B, N, H, W, C, 0))
+    st = _stream(dev)
+    cap = _initial_pairs(B, N, H, W)
+    for _ in range(2):
+        off = torch.empty(B * nT + 1, dtype=torch.int32, device=dev)
+        lst = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        _lib.pdr_splat_bin(params.data_ptr(), B, N, H, W, C, radius, off.data_ptr(),
+                           lst.data_ptr(), cap, ws.ptr, ws.nbytes, st)
+        rc, need = _lib.pdr_splat_check(ws.ptr, st)
+        if rc == _lib.PDR_OK:
+            return off, lst[:need]
+        if rc != _lib.PDR_ERR_OVERFLOW:
+            raise _lib.PdrError(rc, "pdr_splat_bin")
+        cap = need
+    raise _lib.PdrError(_lib.PDR_ERR_OVERFLOW, "pdr_splat_bin")
+
+
+class SplatRender(torch.autograd.Function):
+    """image = render(params); backward reuses the forward's binning."""
+
+    @staticmethod
+    def forward(ctx, params, H, W, radius):
+        params = params.contiguous()
+        image, ws = forward(params, H, W, radius)
+        ctx.save_for_backward(params)
+        ctx.meta = (H, W, radius, ws)
+        return image
+
+    @staticmethod
+    def backward(ctx, grad_image):
+        (params,) = ctx.saved_tensors
+        H, W, radius, ws = ctx.meta
+        g = backward(params, grad_image.contiguous(), H, W, radius, workspace=ws,
+                     reuse_binning=True)
+        return g, None, None, None
+
+
+def render(params: torch.Tensor, H: int, W: int, radius: float = 3.0) -> torch.Tensor:
+    """Differentiable render of [B, N, 5 + C] Gaussians to [B, H, W, C]."""
+    return SplatRender.apply(params, H, W, radius)

@@ -1,0 +1,122 @@
+/*
+ * pdr_splat.h -- C ABI of the MI355X (gfx950) differentiable 2D anisotropic
+ * Gaussian splatting layer.
+ *
+ * The operation ("Learning Video Dynamics with Predictive Differentiable
+ * Rendering": the arXiv abstract gives each Gaussian 5 + C learnable values,
+ * position, scale, rotation and C channel amplitudes, rendered by a
+ * differentiable 2D Gaussian renderer with arbitrary channels; the reading
+ * notes on the paper, sections "Core Idea" and "Method", state that the frame
+ * is the additive accumulation of the Gaussian primitives -- no opacity, no
+ * compositing, no depth order; "Key Insight" and "Limitation" name the kernel
+ * support as a tuned knob):
+ *
+ *   params[b][n] = { mu_x, mu_y, s1, s2, theta, a[0..C-1] }
+ *   p = (x + 1/2, y + 1/2),  d = p - mu,  c = cos theta, s = sin theta
+ *   z1 = ( c dx + s dy) / s1,   z2 = (-s dx + c dy) / s2,   q = z1^2 + z2^2
+ *   w  = exp(-q / 2) if q <= radius^2 else 0
+ *   image[b][y][x][ch] = sum_n a[b][n][ch] * w[b][n](x, y)
+ *
+ * mu is in pixels (x right, y down), s1/s2 are per-axis standard deviations
+ * in pixels, theta is the angle of axis 1 in radians, radius is the
+ * truncation in units of sigma.  A Gaussian is invalid -- contributes nothing
+ * and gets a zero gradient -- if any of its 5 + C values is not finite or if
+ * s1 <= 0 or s2 <= 0.  The backward returns dL/dparams for a given dL/dimage
+ * (the truncation indicator is not differentiated).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers (hipMalloc / torch), fp32 or
+ *    int32, C-contiguous, owned by the caller.  The library never allocates
+ *    or frees device memory; everything it needs lives in the caller's
+ *    workspace.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *    enqueue work and return without synchronising, except pdr_splat_check.
+ *  - Arguments are validated before anything is enqueued; a negative status
+ *    is returned and nothing runs.  Launch failures return PDR_ERR_HIP.
+ *  - Data-dependent failures (list capacity overflow, a stale workspace on
+ *    reuse) are raised on the device into the workspace header and reported
+ *    by pdr_splat_check; outputs of such a call are undefined.
+ *  - Reentrant: concurrent calls need distinct workspaces.
+ */
+#ifndef PDR_SPLAT_H
+#define PDR_SPLAT_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pdr_status {
+    PDR_OK = 0,
+    PDR_ERR_INVALID_ARG = -1, /* null pointer, size < 1, radius not finite or <= 0, H/W too big */
+    PDR_ERR_WORKSPACE = -2,   /* workspace smaller than its fixed part or misaligned */
+    PDR_ERR_HIP = -3,         /* a HIP call or kernel launch failed */
+    PDR_ERR_OVERFLOW = -4,    /* more (tile, Gaussian) pairs than the workspace holds */
+    PDR_ERR_STALE = -5        /* backward asked to reuse binning the workspace does not hold */
+};
+
+/* Tile edge in pixels used by binning and raster (16). */
+int pdr_splat_tile_size(void);
+
+/* Bytes of workspace for a problem and a (tile, Gaussian) pair capacity.
+ * Returns a negative pdr_status on invalid sizes.  The fixed part covers a
+ * 256-byte header, 40 bytes per Gaussian and 8 bytes per tile; every pair
+ * takes 4 more bytes.  max_pairs <= 2^31 - 1. */
+long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long max_pairs);
+
+/* Forward.  params [B][N][5+C] fp32 -> image [B][H][W][C] fp32 (overwritten).
+ * Bins the Gaussians into the workspace (kept for a later backward with
+ * reuse_binning = 1).  H, W <= 32767; B*N and B*H*W*C < 2^31. */
+int pdr_splat_forward(const float *params, float *image, int B, int N, int H, int W, int C,
+                      float radius, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward.  grad_image [B][H][W][C] fp32 -> grad_params [B][N][5+C] fp32
+ * (overwritten: dL/dmu_x, dL/dmu_y, dL/ds1, dL/ds2, dL/dtheta, dL/da[C]).
+ * reuse_binning = 1 uses the lists of the last forward on this workspace;
+ * the workspace records (B, N, H, W, C, radius, params) at binning and a
+ * mismatch is flagged as PDR_ERR_STALE.  The caller must not have changed
+ * the parameter values in between.  reuse_binning = 0 bins again. */
+int pdr_splat_backward(const float *params, const float *grad_image, float *grad_params, int B,
+                       int N, int H, int W, int C, float radius, void *workspace,
+                       size_t workspace_bytes, int reuse_binning, void *stream);
+
+/* Binning only, for inspection: writes tile_off [B*nT + 1] (exclusive scan of
+ * per-tile counts, frame-major, tiles row-major, nT = ceil(W/16)*ceil(H/16))
+ * and tile_list [cap] (per tile, the ascending indices n of Gaussians whose
+ * pixel bounding box meets the tile).  Device pointers.  The list part is
+ * only valid when pdr_splat_check reports PDR_OK and total <= cap. */
+int pdr_splat_bin(const float *params, int B, int N, int H, int W, int C, float radius,
+                  int *tile_off, int *tile_list, long long cap, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/* Synchronises `stream`, then reports the device-side status of the last
+ * call on `workspace`: PDR_OK, PDR_ERR_OVERFLOW or PDR_ERR_STALE (or
+ * PDR_ERR_HIP).  *pairs_needed (may be NULL) receives the pair total of the
+ * last binning. */
+int pdr_splat_check(void *workspace, void *stream, long long *pairs_needed);
+
+/* Static description of a status code. */
+const char *pdr_splat_status_string(int status);
+
+/* Diagnostic per-kernel timing, off by default.  While enabled, each kernel
+ * launched by the entry points above is bracketed by two hipEvents recorded on
+ * the caller's stream (this adds a small host cost per launch).
+ * pdr_splat_timing returns the previous state.  pdr_splat_timing_read waits
+ * for the recorded events and fills total_ms[k] / launches[k] (arrays of
+ * PDR_KERNEL_COUNT, may be NULL) with the accumulated milliseconds and launch
+ * counts per kernel class k; reset != 0 clears the accumulators. */
+enum pdr_kernel_id {
+    PDR_K_PREPROCESS = 0, PDR_K_BIN_COUNT = 1, PDR_K_SCAN = 2, PDR_K_BIN_WRITE = 3,
+    PDR_K_FORWARD_RASTER = 4, PDR_K_ZERO = 5, PDR_K_BACKWARD_RASTER = 6, PDR_K_FINALIZE = 7,
+    PDR_KERNEL_COUNT = 8
+};
+int pdr_splat_timing(int enable);
+int pdr_splat_timing_read(double *total_ms, long long *launches, int reset);
+const char *pdr_splat_kernel_name(int id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDR_SPLAT_H */

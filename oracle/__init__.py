@@ -14,6 +14,8 @@ file's header:
   (pixel, Gaussian) pair with no pruning.
 * ``grad``    -- the analytic backward dL/d(mu, s, theta, a) with slack and
   magnitude per output.
+* ``count_support`` -- per frame, the number of (Gaussian, pixel) pairs
+  inside the truncation (the unit of work the benchmark reports).
 * ``bin``     -- brute-force (tile, Gaussian) overlap lists, ascending
   Gaussian index, and each Gaussian's pixel box.
 """
@@ -61,6 +63,8 @@ def _load():
         lib.orc_grad.restype = ctypes.c_int
         lib.orc_bin.argtypes = [dp, i, i, i, i, i, d, i, i, ip, lp, ip, ctypes.c_longlong, ip]
         lib.orc_bin.restype = ctypes.c_longlong
+        lib.orc_count_support.argtypes = [dp, i, i, i, i, i, d, i, lp]
+        lib.orc_count_support.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -147,3 +151,16 @@ def bin(params, H, W, radius=3.0, tile=16, nthreads=None, with_lists=True):
             raise ValueError("orc_bin failed: %d" % tot2)
         lst = lst[:tot]
     return counts, off, lst, rect
+
+
+def count_support(params, H, W, radius=3.0, nthreads=None):
+    """Return int64 [B]: pairs with q <= k^2 per frame."""
+    p = _params64(params)
+    B, N, P = p.shape
+    pairs = np.zeros(B, np.int64)
+    rc = _load().orc_count_support(_ptr(p, ctypes.c_double), B, N, H, W, P - 5, float(radius),
+                                   int(nthreads or default_threads()),
+                                   _ptr(pairs, ctypes.c_longlong))
+    if rc != 0:
+        raise ValueError("orc_count_support failed: %d" % rc)
+    return pairs

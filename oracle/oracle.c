@@ -391,3 +391,42 @@ long long orc_bin(const double *params, int B, int N, int H, int W, int C, doubl
     for_frames(B, nthreads, bin_frame, &Bn);
     return tot;
 }
+
+/* ------------------------------------------------------------------------ */
+/* support count: pairs with q <= k^2 per frame (no image, no exp)           */
+
+typedef struct {
+    const double *params;
+    int N, H, W, C;
+    double k;
+    long long *pairs;
+} cnt_ctx;
+
+static void cnt_frame(void *p, int b) {
+    cnt_ctx *X = (cnt_ctx *)p;
+    int N = X->N, P = 5 + X->C;
+    double kk = X->k * X->k;
+    const double *gp = X->params + (size_t)b * N * P;
+    long long n_in = 0;
+    for (int n = 0; n < N; n++) {
+        gauss_geo G;
+        geometry(gp + (size_t)n * P, X->C, X->H, X->W, X->k, &G);
+        int xa, xb, ya, yb;
+        if (!scan_box(&G, X->H, X->W, &xa, &xb, &ya, &yb)) continue;
+        for (int y = ya; y <= yb; y++)
+            for (int x = xa; x <= xb; x++) {
+                double z1, z2;
+                if (pixel_q(&G, x, y, &z1, &z2) <= kk) n_in++;
+            }
+    }
+    X->pairs[b] = n_in;
+}
+
+/* pairs [B]: number of (Gaussian, pixel) pairs inside the truncation */
+int orc_count_support(const double *params, int B, int N, int H, int W, int C, double k,
+                      int nthreads, long long *pairs) {
+    if (!params || !pairs || B < 1 || N < 0 || H < 1 || W < 1 || C < 1) return -1;
+    cnt_ctx X = {params, N, H, W, C, k, pairs};
+    for_frames(B, nthreads, cnt_frame, &X);
+    return 0;
+}

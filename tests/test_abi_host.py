@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/pdr_splat.h declares, sizes workspaces as documented
+and rejects invalid arguments before touching a device."""
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from differentiable_gaussian_splatting_pdr_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pdr_splat.h")
+
+FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pdr_splat_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pdr_splat_\w+)", out))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    L = _lib.lib()
+    for f in declared_functions():
+        assert hasattr(L, f)
+
+
+def test_tile_size_and_status_strings():
+    assert _lib.pdr_splat_tile_size() == 16
+    for code in (0, -1, -2, -3, -4, -5):
+        assert _lib.status_string(code) != "unknown status"
+    assert _lib.status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes_layout():
+    def a(v):
+        return (v + 255) // 256 * 256
+    B, N, H, W, C = 384, 4096, 128, 128, 3
+    bt = B * 64
+    fixed = a(256) + a(B * N * 32) + a(B * N * 8) + a(bt * 4) + a((bt + 1) * 4)
+    assert _lib.pdr_splat_workspace_bytes(B, N, H, W, C, 0) == fixed
+    assert _lib.pdr_splat_workspace_bytes(B, N, H, W, C, 1000) == fixed + a(4000)
+    # ragged sizes round the tile grid up
+    assert _lib.pdr_splat_workspace_bytes(1, 10, 17, 33, 1, 0) == (
+        a(256) + a(320) + a(80) + a(3 * 2 * 4) + a(7 * 4))
+
+
+@pytest.mark.parametrize("args", [
+    (0, 10, 16, 16, 1, 0), (1, 0, 16, 16, 1, 0), (1, 10, 0, 16, 1, 0), (1, 10, 16, 0, 1, 0),
+    (1, 10, 16, 16, 0, 0), (1, 10, 16, 16, 1, -1), (1, 10, 40000, 16, 1, 0),
+    (1, 10, 16, 16, 1, 2 ** 31), (1 << 20, 1 << 12, 16, 16, 1, 0),
+])
+def test_workspace_bytes_rejects(args):
+    with pytest.raises(_lib.PdrError) as e:
+        _lib.pdr_splat_workspace_bytes(*args)
+    assert e.value.status == _lib.PDR_ERR_INVALID_ARG
+
+
+def _fwd(**kw):
+    a = dict(params=FAKE, image=FAKE, B=1, N=4, H=16, W=16, C=1, radius=3.0,
+             workspace=FAKE, workspace_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return _lib.lib().pdr_splat_forward(a["params"], a["image"], a["B"], a["N"], a["H"], a["W"],
+                                        a["C"], a["radius"], a["workspace"], a["workspace_bytes"],
+                                        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(params=None), -1), (dict(image=None), -1), (dict(B=0), -1), (dict(N=-3), -1),
+    (dict(C=0), -1), (dict(W=40000), -1), (dict(radius=0.0), -1), (dict(radius=-1.0), -1),
+    (dict(radius=math.nan), -1), (dict(radius=math.inf), -1), (dict(workspace=None), -1),
+    (dict(workspace=FAKE + 4), -2), (dict(workspace_bytes=100), -2),
+])
+def test_forward_validates_before_launch(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_backward_and_bin_validate():
+    L = _lib.lib()
+    assert L.pdr_splat_backward(FAKE, None, FAKE, 1, 4, 16, 16, 1, 3.0, FAKE, 1 << 20, 1, None) == -1
+    assert L.pdr_splat_backward(FAKE, FAKE, FAKE, 1, 4, 16, 16, 1, float("nan"), FAKE, 1 << 20, 1,
+                                None) == -1
+    assert L.pdr_splat_backward(FAKE, FAKE, FAKE, 1, 4, 16, 16, 1, 3.0, FAKE, 10, 0, None) == -2
+    assert L.pdr_splat_bin(FAKE, 1, 4, 16, 16, 1, 3.0, FAKE, FAKE, -1, FAKE, 1 << 20, None) == -1
+    assert L.pdr_splat_bin(FAKE, 1, 4, 16, 16, 1, 3.0, None, FAKE, 5, FAKE, 1 << 20, None) == -1
+    assert L.pdr_splat_check(None, None, None) == -1
+
+
+def test_timing_toggle_without_device():
+    assert _lib.pdr_splat_timing(True) is False
+    assert _lib.pdr_splat_timing(False) is True
+    t = _lib.pdr_splat_timing_read(reset=True)
+    assert set(t) == {"preprocess", "bin_count", "scan", "bin_write", "forward_raster",
+                      "zero_verify", "backward_raster", "finalize"}
+    assert all(v == (0.0, 0) for v in t.values())

@@ -154,6 +154,15 @@ def test_allpairs_equals_box_scatter(orc):
     assert np.array_equal(a, b)
 
 
+def test_support_count_matches_render(orc):
+    _, p, _ = workloads.make_inputs(2, frames=3, with_grad=False)
+    _, _, _, pairs = orc.render(p, 128, 128)
+    assert np.array_equal(orc.count_support(p, 128, 128), pairs)
+    p2, _ = workloads.make_custom(2, 40, 20, 30, 1, seed=9, mean_margin=5)
+    img, _, _, pairs2 = orc.render(p2, 20, 30, allpairs=True)
+    assert np.array_equal(orc.count_support(p2, 20, 30), pairs2)
+
+
 def test_invalid_gaussians_are_culled(orc):
     p, g = workloads.make_custom(1, 8, 20, 20, 2, seed=2)
     p = p.astype(np.float64)
