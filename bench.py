@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-loop", type=int, default=0,
                     help="only run this many steps (for rocprofv3), print nothing else")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="with --profile-loop: also run one device-to-device copy of this many "
+                         "MiB, the reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -150,6 +153,12 @@ def main():
     if args.profile_loop:
         for _ in range(args.profile_loop):
             step()
+        if args.calib_copy_mb:
+            n = args.calib_copy_mb << 20
+            src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
         torch.cuda.synchronize()
         print("profile loop done: %d steps" % args.profile_loop, flush=True)
         return
