@@ -34,10 +34,10 @@ def flops_per_pair(C):
     return 12 + 2 * C, 24 + 4 * C
 
 
-def kernel_bytes(B, N, H, W, C, pairs_tiles):
+def kernel_bytes(B, N, H, W, C, pairs_tiles, T):
     """Algorithmic HBM bytes per launch of each kernel (each tensor moved once)."""
     BN, img = B * N, B * H * W * C * 4
-    nT = ((H + 15) // 16) * ((W + 15) // 16)
+    nT = ((H + T - 1) // T) * ((W + T - 1) // T)
     P = 5 + C
     return {
         "preprocess": BN * P * 4 + BN * 40,
@@ -128,7 +128,8 @@ def main():
 
     # exact list capacity from one binning pass
     ws_fixed = _lib.pdr_splat_workspace_bytes(B, N, H, W, C, 0)
-    nT = ((H + 15) // 16) * ((W + 15) // 16)
+    T = _lib.pdr_splat_tile_size()
+    nT = ((H + T - 1) // T) * ((W + T - 1) // T)
     probe = torch.empty(ws_fixed, dtype=torch.uint8, device=dev)
     off = torch.empty(B * nT + 1, dtype=torch.int32, device=dev)
     lst = torch.empty(1, dtype=torch.int32, device=dev)
@@ -200,7 +201,7 @@ def main():
 
     f_fwd, f_bwd = flops_per_pair(C)
     kernels = {}
-    kb = kernel_bytes(B, N, H, W, C, tile_pairs)
+    kb = kernel_bytes(B, N, H, W, C, tile_pairs, T)
     for name, (tot_ms, cnt) in per_kernel.items():
         if cnt == 0:
             continue

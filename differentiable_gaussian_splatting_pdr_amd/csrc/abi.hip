@@ -13,13 +13,14 @@ using namespace pdr;
 namespace {
 
 struct Dims {
-  long long BN, BT;
+  long long BN, BT, BR;
   int nTx, nTy;
 };
 
 int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
   if (B < 1 || N < 1 || H < 1 || W < 1 || C < 1) return PDR_ERR_INVALID_ARG;
   if (H > kMaxHW || W > kMaxHW || N > kMaxN) return PDR_ERR_INVALID_ARG;
+  if ((W + kTile - 1) / kTile > kMaxGroupTiles) return PDR_ERR_INVALID_ARG;  // one tile row per bin group
   long long BN = (long long)B * N;
   if (BN > 0x7fffffffLL || BN * (5 + C) > 0x7fffffffffffLL) return PDR_ERR_INVALID_ARG;
   if ((long long)B * H * W * C > (1LL << 46)) return PDR_ERR_INVALID_ARG;
@@ -27,6 +28,7 @@ int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
   d->nTy = (H + kTile - 1) / kTile;
   d->BN = BN;
   d->BT = (long long)B * d->nTx * d->nTy;
+  d->BR = (long long)B * d->nTy;
   if (d->BT + 1 > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
   return PDR_OK;
 }
@@ -40,11 +42,11 @@ int validate_radius(float radius) {
 int layout_for(const Dims &d, void *ws, size_t bytes, Layout *L) {
   if (!ws) return PDR_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return PDR_ERR_WORKSPACE;
-  Layout fixed = make_layout(d.BN, d.BT, 0);
+  Layout fixed = make_layout(d.BN, d.BT, d.BR, 0);
   if (bytes < fixed.list) return PDR_ERR_WORKSPACE;
   long long cap = (long long)((bytes - fixed.list) / 4);
   if (cap > 0x7fffffffLL) cap = 0x7fffffffLL;
-  *L = make_layout(d.BN, d.BT, cap);
+  *L = make_layout(d.BN, d.BT, d.BR, cap);
   L->total = bytes;
   return PDR_OK;
 }
@@ -62,7 +64,7 @@ long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long
   int rc = validate_sizes(B, N, H, W, C, &d);
   if (rc != PDR_OK) return rc;
   if (max_pairs < 0 || max_pairs > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
-  return (long long)make_layout(d.BN, d.BT, max_pairs).total;
+  return (long long)make_layout(d.BN, d.BT, d.BR, max_pairs).total;
 }
 
 int pdr_splat_forward(const float *params, float *image, int B, int N, int H, int W, int C,

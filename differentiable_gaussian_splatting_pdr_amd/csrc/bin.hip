@@ -3,8 +3,6 @@
 //  k_preprocess   one thread per Gaussian: validity, fp64 pixel bounding box
 //                 of the truncated ellipse q <= k^2, whitening rows.
 //  k_bin<false>   per (frame, tile group): per-tile overlap counts.
-//  k_scan         one workgroup: exclusive scan of the counts (wave64 DPP
-//                 scan) -> tile offsets, pair total, overflow flag.
 //  k_bin<true>    per (frame, tile group): the per-tile lists, ascending
 //                 Gaussian index, at the scanned offsets.
 //
@@ -94,29 +92,89 @@ __global__ __launch_bounds__(256) void k_preprocess(const float *__restrict__ pa
   boxes[i] = make_uint2(r.bx, r.by);
 }
 
-// LDS bit matrix binning.  Grid: (groups per frame, B); 256 threads.
-// Dynamic LDS: Tg * (NC / 32) words, NC a multiple of 64.
+// Sum of a long long over the workgroup (all threads receive it).
+__device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  const int tid = threadIdx.x;
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  long long t = 0;
+  for (int w = 0; w < kBinThreads / kWave; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// LDS bit matrix binning.  Grid: (groups per frame G, frames B); a group is
+// a band of gh whole tile rows.  Dynamic LDS: Tg * (NC / 32) words, NC a
+// multiple of 64.
+//
+// Count pass (WRITE = false): per-tile counts and the group's total.
+// Write pass (WRITE = true): the group's base offset is the sum of the
+// totals of all groups before it (frame-major, bands top to bottom); an
+// exclusive scan (wave64 DPP scan) of its tiles' counts gives their
+// offsets; then the lists are written.  The last group writes the pair
+// total and the overflow flag.
 template <bool WRITE>
-__global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ boxes, int N,
-                                                     int nTx, int nTy, int gw, int gh, int ngx,
-                                                     int NC, int *__restrict__ counts,
-                                                     const int *__restrict__ tile_off,
-                                                     int *__restrict__ list, const WsHeader *hdr) {
+__global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ boxes, int B, int N,
+                                                     int nTx, int nTy, int gh, int G, int NC,
+                                                     int *__restrict__ counts,
+                                                     int *__restrict__ gtot,
+                                                     int *__restrict__ tile_off,
+                                                     int *__restrict__ list, long long cap,
+                                                     WsHeader *hdr) {
   extern __shared__ unsigned int bits[];
   __shared__ int base[kMaxGroupTiles];
-  const int b = blockIdx.y;
-  const int gx = blockIdx.x % ngx, gy = blockIdx.x / ngx;
-  const int tx0 = gx * gw, ty0 = gy * gh;
-  const int aw = min(gw, nTx - tx0), ah = min(gh, nTy - ty0);
-  const int Tg = aw * ah;
+  __shared__ long long red[kBinThreads / kWave];
+  __shared__ int wtot[kBinThreads / kWave];
+  const int b = blockIdx.y, g = blockIdx.x;
+  const int ty0 = g * gh;
+  const int ah = min(gh, nTy - ty0);
+  const int Tg = nTx * ah;
   const int nT = nTx * nTy;
+  const size_t t0 = (size_t)b * nT + (size_t)ty0 * nTx;  // first tile of the group
   const int words = NC >> 5;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (WRITE && (hdr->status & kStatusOverflow)) return;
-  for (int lt = tid; lt < Tg; lt += kBinThreads) {
-    int t = (ty0 + lt / aw) * nTx + tx0 + lt % aw;
-    base[lt] = WRITE ? tile_off[(size_t)b * nT + t] : 0;
+
+  if (WRITE) {
+    // base of this group: totals of all groups before it
+    const long long gi = (long long)b * G + g;
+    long long part = 0;
+    for (long long k = tid; k < gi; k += kBinThreads) part += gtot[k];
+    const long long gbase = block_sum_ll(part, red);
+    // exclusive scan of the group's tile counts (2 * kBinThreads >= Tg)
+    const int c0 = 2 * tid < Tg ? counts[t0 + 2 * tid] : 0;
+    const int c1 = 2 * tid + 1 < Tg ? counts[t0 + 2 * tid + 1] : 0;
+    const int incl = wave_incl_scan(c0 + c1);
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int wex = 0, gsum = 0;
+    for (int w = 0; w < kBinThreads / kWave; ++w) {
+      wex += w < wave ? wtot[w] : 0;
+      gsum += wtot[w];
+    }
+    const long long e0 = gbase + wex + incl - (c0 + c1);
+    if (2 * tid < Tg) {
+      tile_off[t0 + 2 * tid] = (int)min(e0, 0x7fffffffLL);
+      base[2 * tid] = (int)min(e0, 0x7fffffffLL);
+    }
+    if (2 * tid + 1 < Tg) {
+      tile_off[t0 + 2 * tid + 1] = (int)min(e0 + c0, 0x7fffffffLL);
+      base[2 * tid + 1] = (int)min(e0 + c0, 0x7fffffffLL);
+    }
+    const long long gend = gbase + gsum;
+    const bool limit = gend > cap || gend > 0x7fffffffLL;
+    if (tid == 0 && b == B - 1 && g == G - 1) {
+      // a fresh binning: clears any earlier overflow or stale flag
+      tile_off[(size_t)B * nT] = (int)min(gend, 0x7fffffffLL);
+      hdr->total = gend;
+      hdr->cap = cap;
+      hdr->status = limit ? kStatusOverflow : 0;
+    }
+    if (limit) return;  // uniform: this group's lists do not fit
+  } else {
+    for (int lt = tid; lt < Tg; lt += kBinThreads) base[lt] = 0;
   }
+
   const uint2 *fb = boxes + (size_t)b * N;
   for (int c0 = 0; c0 < N; c0 += NC) {
     for (int w = tid; w < Tg * words; w += kBinThreads) bits[w] = 0u;
@@ -127,16 +185,16 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
       int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
       int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
       if (x0 > x1) continue;
-      int ux0 = max(x0 / kTile, tx0), ux1 = min(x1 / kTile, tx0 + aw - 1);
-      int uy0 = max(y0 / kTile, ty0), uy1 = min(y1 / kTile, ty0 + ah - 1);
+      int ux0 = x0 >> kTileShift, ux1 = x1 >> kTileShift;
+      int uy0 = max(y0 >> kTileShift, ty0), uy1 = min(y1 >> kTileShift, ty0 + ah - 1);
       const unsigned int bit = 1u << (i & 31);
       const int wi = i >> 5;
       for (int ty = uy0; ty <= uy1; ++ty)
         for (int tx = ux0; tx <= ux1; ++tx)
-          atomicOr(&bits[((ty - ty0) * aw + (tx - tx0)) * words + wi], bit);
+          atomicOr(&bits[((ty - ty0) * nTx + tx) * words + wi], bit);
     }
     __syncthreads();
-    // compaction: a wave owns tiles wave, wave + 4, ...
+    // compaction: a wave owns tiles wave, wave + 8, ...
     for (int lt = wave; lt < Tg; lt += kBinThreads / kWave) {
       int run = base[lt];
       const unsigned int *row = bits + (size_t)lt * words;
@@ -162,81 +220,39 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
     __syncthreads();
   }
   if (!WRITE) {
+    long long part = 0;
     for (int lt = tid; lt < Tg; lt += kBinThreads) {
-      int t = (ty0 + lt / aw) * nTx + tx0 + lt % aw;
-      counts[(size_t)b * nT + t] = base[lt];
+      counts[t0 + lt] = base[lt];
+      part += base[lt];
     }
-  }
-}
-
-// Exclusive scan of M int32 counts by one 1024-thread workgroup, 4096
-// counts per step: thread-serial over 4, wave64 DPP scan, the 16 wave
-// totals and the running carry combined in 64 bits by one thread.
-__global__ __launch_bounds__(kScanThreads) void k_scan(const int *__restrict__ counts, long long M,
-                                                       int *__restrict__ tile_off, long long cap,
-                                                       WsHeader *hdr) {
-  __shared__ long long wsum[kScanThreads / kWave];
-  __shared__ long long carry_s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (long long base = 0; base < M; base += 4 * kScanThreads) {
-    long long idx = base + 4LL * tid;
-    int v[4];
-    for (int j = 0; j < 4; ++j) v[j] = (idx + j < M) ? counts[idx + j] : 0;
-    int tsum = v[0] + v[1] + v[2] + v[3];
-    int incl = wave_incl_scan(tsum);
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    if (tid == 0) {
-      // 16 wave totals: a serial exclusive scan in one lane, exact in 64 bits
-      long long run = carry_s;
-      for (int w = 0; w < kScanThreads / kWave; ++w) {
-        long long t = wsum[w];
-        wsum[w] = run;
-        run += t;
-      }
-      carry_s = run;
-    }
-    __syncthreads();
-    long long off = wsum[wave] + (incl - tsum);
-    for (int j = 0; j < 4; ++j) {
-      if (idx + j < M) tile_off[idx + j] = (int)off;
-      off += v[j];
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    long long tot = carry_s;
-    tile_off[M] = (int)(tot > 0x7fffffffLL ? 0x7fffffffLL : tot);
-    hdr->total = tot;
-    hdr->cap = cap;
-    // a fresh binning: clears any earlier overflow or stale flag
-    int st = 0;
-    if (tot > cap || tot > 0x7fffffffLL) st |= kStatusOverflow;
-    hdr->status = st;
+    const long long tot = block_sum_ll(part, red);
+    if (tid == 0) gtot[(size_t)b * G + g] = (int)min(tot, 0x7fffffffLL);
   }
 }
 
 // ----------------------------------------------------------------------------
 // host launchers
 
-static void choose_groups(int N, int nTx, int nTy, int *gw, int *gh, int *NC) {
+// Tile groups: bands of whole tile rows whose bit rows (Tg x NC bits) fit
+// the LDS budget; within that, frames are split into more bands so that the
+// grid has about kBinTargetGroups workgroups (every band rescans the frame's
+// boxes, which stay in L2).
+static void choose_groups(int B, int N, int nTx, int nTy, int *gh, int *NC) {
   long long nc = ((long long)N + 63) / 64 * 64;
   if (nc > kMaxChunk) nc = kMaxChunk;
+  const long long bits = kBinLdsBytes * 8LL;
+  const long long row_max = bits / nTx / 64 * 64;  // a full tile row must fit
+  if (nc > row_max) nc = row_max;
   *NC = (int)nc;
-  int tmax = (int)((kBinLdsBytes * 8LL) / nc);  // tiles whose bit rows fit the LDS budget
-  if (tmax > kMaxGroupTiles) tmax = kMaxGroupTiles;
-  if (nTx * nTy <= tmax) {
-    *gw = nTx;
-    *gh = nTy;
-  } else if (nTx <= tmax) {
-    *gw = nTx;
-    *gh = tmax / nTx;
-  } else {
-    *gw = tmax;
-    *gh = 1;
+  long long rows = bits / (nc * nTx);
+  if (rows > kMaxGroupTiles / nTx) rows = kMaxGroupTiles / nTx;
+  if (rows > nTy) rows = nTy;
+  int want = (int)((kBinTargetGroups + B - 1) / B);  // bands per frame for a full grid
+  if (want > 1) {
+    int r = (nTy + want - 1) / want;
+    if (r < rows) rows = r;
   }
+  *gh = rows < 1 ? 1 : (int)rows;
 }
 
 hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C, float radius,
@@ -247,29 +263,25 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   GRec *recs = (GRec *)(w + L.recs);
   uint2 *boxes = (uint2 *)(w + L.boxes);
   int *counts = (int *)(w + L.counts);
+  int *gtot = (int *)(w + L.gtot);
   long long BN = (long long)B * N;
   int nTx = (W + kTile - 1) / kTile, nTy = (H + kTile - 1) / kTile;
   PDR_TIMED(PDR_K_PREPROCESS, st,
             hipLaunchKernelGGL(k_preprocess, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,
                                params, (int)BN, C, H, W, radius, recs, boxes, hdr, N,
                                stamp_valid ? (unsigned long long)(uintptr_t)params : 0ull));
-  int gw, gh, NC;
-  choose_groups(N, nTx, nTy, &gw, &gh, &NC);
-  int ngx = (nTx + gw - 1) / gw, ngy = (nTy + gh - 1) / gh;
-  size_t lds = (size_t)gw * gh * (NC / 32) * 4;
-  dim3 grid((unsigned)(ngx * ngy), (unsigned)B);
+  int gh, NC;
+  choose_groups(B, N, nTx, nTy, &gh, &NC);
+  int G = (nTy + gh - 1) / gh;
+  size_t lds = (size_t)nTx * gh * (NC / 32) * 4;
+  dim3 grid((unsigned)G, (unsigned)B);
   PDR_TIMED(PDR_K_BIN_COUNT, st,
-            hipLaunchKernelGGL(k_bin<false>, grid, dim3(kBinThreads), lds, st, boxes, N, nTx, nTy,
-                               gw, gh, ngx, NC, counts, (const int *)nullptr, (int *)nullptr,
-                               (const WsHeader *)hdr));
-  long long M = (long long)B * nTx * nTy;
-  PDR_TIMED(PDR_K_SCAN, st,
-            hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, st, (const int *)counts, M,
-                               tile_off, cap, hdr));
+            hipLaunchKernelGGL(k_bin<false>, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx,
+                               nTy, gh, G, NC, counts, gtot, (int *)nullptr, (int *)nullptr, cap,
+                               hdr));
   PDR_TIMED(PDR_K_BIN_WRITE, st,
-            hipLaunchKernelGGL(k_bin<true>, grid, dim3(kBinThreads), lds, st, boxes, N, nTx, nTy,
-                               gw, gh, ngx, NC, counts, (const int *)tile_off, list,
-                               (const WsHeader *)hdr));
+            hipLaunchKernelGGL(k_bin<true>, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx,
+                               nTy, gh, G, NC, counts, gtot, tile_off, list, cap, hdr));
   return hipGetLastError();
 }
 

@@ -7,10 +7,10 @@
 
 namespace pdr {
 
-constexpr int kTile = 16;        // tile edge in pixels (binning and raster)
+constexpr int kTileShift = 4;
+constexpr int kTile = 1 << kTileShift;  // tile edge in pixels (binning and raster)
 constexpr int kWave = 64;        // CDNA wavefront width
-constexpr int kBinThreads = 256; // binning workgroup
-constexpr int kScanThreads = 1024;
+constexpr int kBinThreads = 512; // binning workgroup
 constexpr int kMaxHW = 32767;    // pixel boxes are packed as 16-bit coordinates
 constexpr int kMaxN = 1 << 22;   // per-frame Gaussian count bound of the scan's int32 partials
 
@@ -47,19 +47,22 @@ constexpr unsigned int kEmptyBox = 0x0000FFFFu;  // x0 = 65535 > x1 = 0
 
 // Workspace carve-up; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t hdr, recs, boxes, counts, tile_off, list, total;
+  size_t hdr, recs, boxes, counts, gtot, tile_off, list, total;
   long long cap;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-inline Layout make_layout(long long BN, long long BT, long long cap) {
+// BR: tile rows of the batch (B * ceil(H / tile)), an upper bound on the
+// binning's row bands.
+inline Layout make_layout(long long BN, long long BT, long long BR, long long cap) {
   Layout L;
   size_t o = 0;
   L.hdr = o;       o += align256(sizeof(WsHeader));
   L.recs = o;      o += align256(size_t(BN) * sizeof(GRec));
   L.boxes = o;     o += align256(size_t(BN) * 8);
   L.counts = o;    o += align256(size_t(BT) * 4);
+  L.gtot = o;      o += align256(size_t(BR) * 4);
   L.tile_off = o;  o += align256(size_t(BT + 1) * 4);
   L.list = o;      o += align256(size_t(cap) * 4);
   L.total = o;

@@ -18,7 +18,8 @@ void timing_end(int kid, hipStream_t st);
   } while (0)
 
 constexpr int kMaxGroupTiles = 1024;    // tiles of one binning group (static LDS bases)
-constexpr long long kMaxChunk = 16384;  // Gaussians per binning chunk (bit-matrix columns)
+constexpr long long kMaxChunk = 4096;   // Gaussians per binning chunk (bit-matrix columns)
+constexpr long long kBinTargetGroups = 2048;  // binning workgroups to aim for
 constexpr long long kBinLdsBytes = 60 * 1024;  // + 4 KB of static bases stays within 64 KB
 
 // K1 + count + scan + list write; tile_off/list may be the workspace's own

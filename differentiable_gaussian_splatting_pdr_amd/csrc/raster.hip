@@ -1,122 +1,164 @@
 // raster.hip -- forward and backward tile rasterisation of the truncated
 // anisotropic Gaussians, and the gradient finalisation.
 //
-// One wave64 workgroup per 16x16 tile.  Lane l owns the four pixels
-// (x, y) = (l % 16, l / 16 + 4k), k = 0..3, of the tile, i.e. one pixel in
-// each of four 16x4 strips.  The tile's Gaussian list is walked in batches of
-// 64: each lane stages one Gaussian's record and amplitudes in LDS, then the
-// wave reads them back one by one (broadcast).  Strips the Gaussian's pixel
-// box misses are skipped with a scalar branch.
+// A 16x16 tile is covered by units of 64 pixels, UW x UH with UW * UH = 64
+// (16x4 strips or 8x8 quads).  A wave64 owns UX x UY units (a region of
+// UX*UW x UY*UH pixels); lane l owns pixel (l % UW, l / UW) of every one of
+// its units, so a lane holds UX*UY pixels.  The waves of a workgroup cover
+// the tile and share one LDS staging area: batches of
+// the tile's Gaussian list (record + amplitudes) are loaded cooperatively,
+// then every wave reads them back one by one (broadcast).  For each Gaussian
+// a wave skips, with scalar branches, its units the Gaussian's pixel box
+// misses.
 //
 // Per (Gaussian, pixel): z = L (p - mu) with L the whitening rows scaled by
 // sqrt(log2(e)/2), q' = z1^2 + z2^2, w = exp2(-q') if q' <= k^2 log2(e)/2.
-// This equals exp(-q/2) with the Mahalanobis q of the definition.
+// This equals exp(-q/2) with the Mahalanobis q of the definition.  Moving
+// by whole units is linear: z(p + (i UW, j UH)) = z(p) + i UW L e_x +
+// j UH L e_y, evaluated with one fma per component.
 //
 // Forward: C channel accumulators per pixel in registers.
 // Backward: per lane the partial sums over its pixels of
 //   A_c = G_c w,  S1 = v z1, S2 = v z2, S11 = v z1^2, S22 = v z2^2, S12 = v z1 z2
-// (v = w sum_c G_c a_c, z unscaled by 1/kappa), reduced across the wave by a
-// transposed butterfly (each exchange halves the values a lane carries) so
-// that after log2(K) steps every lane holds one sum; one global fp32 atomic
-// per wave per Gaussian per sum then lands in grad_params, and a finalise
-// kernel applies the chain rule in place.
+// (v = w sum_c G_c a_c, z in the scaled coordinates); a unit whose pixels
+// all fall outside the truncation is skipped after the compare (wave
+// ballot).  The sums are reduced across the wave by a transposed butterfly
+// (each exchange halves the values a lane carries) so that after log2(K)
+// steps every lane holds one total; one global fp32 atomic per wave per
+// Gaussian per sum lands in grad_params, and a finalise kernel applies the
+// chain rule in place.
 #include "pdr_common.hpp"
 #include "pdr_internal.hpp"
 
 namespace pdr {
 
-template <int CP>
-struct BatchLds {
-  GRec rec[kWave];
-  float amp[kWave][CP];
-  int idx[kWave];
+template <int UW, int UX, int UY>
+struct WaveLayout {
+  static constexpr int kUH = kWave / UW;
+  static constexpr int kRW = UX * UW, kRH = UY * kUH;  // wave region
+  static_assert(kRW == kTile && kTile % kRH == 0, "a wave spans the tile's width");
+  static constexpr int kWaves = kTile / kRH;
+  static constexpr int kUnitsPerWave = UX * UY;  // consecutive bits of the tile's unit mask
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kBatch = kThreads;  // list entries staged per round
 };
 
-template <int CP>
-__device__ __forceinline__ void stage_batch(BatchLds<CP> &s, const GRec *__restrict__ recs,
+template <int CP, int NB>
+struct BatchLds {
+  GRec rec[NB];
+  float amp[NB][CP];
+  unsigned int mask[NB];  // tile units (row-major) the Gaussian's pixel box meets
+  int gidx[NB];           // frame * N + n
+};
+
+// One list entry per thread of the workgroup: record, amplitudes, and the
+// mask of tile units its pixel box meets (computed here, in parallel, so
+// the per-entry loop only tests bits).
+template <int CP, int NB, int UW>
+__device__ __forceinline__ void stage_batch(BatchLds<CP, NB> &s, const GRec *__restrict__ recs,
                                             const float *__restrict__ params,
                                             const int *__restrict__ list, int s0, int cnt,
-                                            size_t gbase, int P, int c0, int cc, int lane) {
-  if (lane < cnt) {
-    int n = list[s0 + lane];
-    s.idx[lane] = n;
-    s.rec[lane] = recs[gbase + n];
+                                            size_t gbase, int P, int c0, int cc, int tid,
+                                            int tx0, int ty0) {
+  constexpr int UH = kWave / UW, NUX = kTile / UW, NUY = kTile / UH;
+  if (tid < cnt) {
+    const int n = list[s0 + tid];
+    const GRec r = recs[gbase + n];
+    s.gidx[tid] = (int)gbase + n;
+    s.rec[tid] = r;
     const float *a = params + (gbase + n) * (size_t)P + 5 + c0;
 #pragma unroll
-    for (int c = 0; c < CP; ++c) s.amp[lane][c] = c < cc ? a[c] : 0.f;
+    for (int c = 0; c < CP; ++c) s.amp[tid][c] = c < cc ? a[c] : 0.f;
+    // listed => the box meets the tile; clamp it to the tile's units
+    const int ux0 = max(0, ((int)(r.bx & 0xffffu) - tx0) / UW);
+    const int ux1 = min(NUX - 1, ((int)(r.bx >> 16) - tx0) / UW);
+    const int uy0 = max(0, ((int)(r.by & 0xffffu) - ty0) / UH);
+    const int uy1 = min(NUY - 1, ((int)(r.by >> 16) - ty0) / UH);
+    const unsigned int row = ((2u << ux1) - 1u) & ~((1u << ux0) - 1u);
+    unsigned int m = 0u;
+#pragma unroll
+    for (int j = 0; j < NUY; ++j)
+      if (j >= uy0 && j <= uy1) m |= row << (j * NUX);
+    s.mask[tid] = m;
   }
 }
 
-// strips k (rows ystrip0 + 4k .. + 3) met by the box rows [y0, y1]
-__device__ __forceinline__ void strip_range(unsigned int by, int ystrip0, int *k0, int *k1) {
-  int y0 = (int)(by & 0xffffu), y1 = (int)(by >> 16);
-  *k0 = max(0, (y0 - ystrip0) >> 2);
-  *k1 = min(3, (y1 - ystrip0) >> 2);
-}
-
-template <int CP>
-__global__ __launch_bounds__(kWave) void k_forward(const GRec *__restrict__ recs,
-                                                   const float *__restrict__ params,
-                                                   const int *__restrict__ tile_off,
-                                                   const int *__restrict__ list, int B, int N,
-                                                   int H, int W, int C, int c0, int cc, float thr,
-                                                   int nTx, int nT, float *__restrict__ image,
-                                                   const WsHeader *hdr) {
+template <int CP, int UW, int UX, int UY>
+__global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
+    const GRec *__restrict__ recs, const float *__restrict__ params,
+    const int *__restrict__ tile_off, const int *__restrict__ list, int B, int N, int H, int W,
+    int C, int c0, int cc, float thr, int nTx, int nT, float *__restrict__ image,
+    const WsHeader *hdr) {
+  using WL = WaveLayout<UW, UX, UY>;
+  constexpr int UH = WL::kUH;
   int f, t;
   if (!xcd_frame_item(blockIdx.x, nT, B, &f, &t)) return;
   if (hdr->status & kStatusOverflow) return;
-  __shared__ BatchLds<CP> s;
-  const int lane = threadIdx.x;
-  const int tx = t % nTx, ty = t / nTx;
-  const int px = tx * kTile + (lane & 15);
-  const int py0 = ty * kTile + (lane >> 4);
-  const int ystrip0 = ty * kTile;
-  const float fx = (float)px + 0.5f, fy = (float)py0 + 0.5f;
+  __shared__ BatchLds<CP, WL::kBatch> s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
+  const int tx0 = (t % nTx) * kTile, ty0 = (t / nTx) * kTile;
+  const int rx0 = tx0, ry0 = ty0 + wave * WL::kRH;
+  const int mshift = wave * WL::kUnitsPerWave;
+  const int lx = lane % UW, ly = lane / UW;
+  const float fx = (float)(rx0 + lx) + 0.5f, fy = (float)(ry0 + ly) + 0.5f;
   const int P = 5 + C;
   const size_t gbase = (size_t)f * N;
-  float acc[4][CP];
+  float acc[UY][UX][CP];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int j = 0; j < UY; ++j)
 #pragma unroll
-    for (int c = 0; c < CP; ++c) acc[k][c] = 0.f;
+    for (int i = 0; i < UX; ++i)
+#pragma unroll
+      for (int c = 0; c < CP; ++c) acc[j][i][c] = 0.f;
 
   const int beg = tile_off[(size_t)f * nT + t], end = tile_off[(size_t)f * nT + t + 1];
-  for (int s0 = beg; s0 < end; s0 += kWave) {
-    const int cnt = min(kWave, end - s0);
+  for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
+    const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
-    stage_batch<CP>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, lane);
+    stage_batch<CP, WL::kBatch, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0,
+                                    ty0);
     __syncthreads();
-    for (int j = 0; j < cnt; ++j) {
-      const GRec r = s.rec[j];
-      int k0, k1;
-      strip_range(__builtin_amdgcn_readfirstlane(r.by), ystrip0, &k0, &k1);
+    for (int e = 0; e < cnt; ++e) {
+      const unsigned int um =
+          (__builtin_amdgcn_readfirstlane(s.mask[e]) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+      if (um == 0u) continue;
+      const GRec r = s.rec[e];
       const float dx = fx - r.mx, dy = fy - r.my;
       const float z1 = r.l11 * dx + r.l12 * dy;
       const float z2 = r.l21 * dx + r.l22 * dy;
-      const float st1 = 4.f * r.l12, st2 = 4.f * r.l22;
       float a[CP];
 #pragma unroll
-      for (int c = 0; c < CP; ++c) a[c] = s.amp[j][c];
+      for (int c = 0; c < CP; ++c) a[c] = s.amp[e][c];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (k < k0 || k > k1) continue;
-        const float u1 = z1 + (float)k * st1;
-        const float u2 = z2 + (float)k * st2;
-        const float q = u1 * u1 + u2 * u2;
-        const float w = q <= thr ? __builtin_amdgcn_exp2f(-q) : 0.f;
+      for (int j = 0; j < UY; ++j) {
+        if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
+        const float zr1 = j ? fmaf((float)(UH * j), r.l12, z1) : z1;
+        const float zr2 = j ? fmaf((float)(UH * j), r.l22, z2) : z2;
 #pragma unroll
-        for (int c = 0; c < CP; ++c) acc[k][c] += a[c] * w;
+        for (int i = 0; i < UX; ++i) {
+          if (!(um & (1u << (j * UX + i)))) continue;
+          const float u1 = i ? fmaf((float)(UW * i), r.l11, zr1) : zr1;
+          const float u2 = i ? fmaf((float)(UW * i), r.l21, zr2) : zr2;
+          const float q = u1 * u1 + u2 * u2;
+          const float w = q <= thr ? __builtin_amdgcn_exp2f(-q) : 0.f;
+#pragma unroll
+          for (int c = 0; c < CP; ++c) acc[j][i][c] += a[c] * w;
+        }
       }
     }
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int py = py0 + 4 * k;
-    if (px < W && py < H) {
-      float *o = image + (((size_t)f * H + py) * W + px) * (size_t)C + c0;
+  for (int j = 0; j < UY; ++j) {
 #pragma unroll
-      for (int c = 0; c < CP; ++c)
-        if (c < cc) o[c] = acc[k][c];
+    for (int i = 0; i < UX; ++i) {
+      const int px = rx0 + UW * i + lx, py = ry0 + UH * j + ly;
+      if (px < W && py < H) {
+        float *o = image + (((size_t)f * H + py) * W + px) * (size_t)C + c0;
+#pragma unroll
+        for (int c = 0; c < CP; ++c)
+          if (c < cc) o[c] = acc[j][i][c];
+      }
     }
   }
 }
@@ -164,38 +206,42 @@ struct Pow2Up {
   static constexpr int value = K <= 8 ? 8 : (K <= 16 ? 16 : 32);
 };
 
-template <int CP>
-__global__ __launch_bounds__(kWave) void k_backward(const GRec *__restrict__ recs,
-                                                    const float *__restrict__ params,
-                                                    const float *__restrict__ gimg,
-                                                    const int *__restrict__ tile_off,
-                                                    const int *__restrict__ list, int B, int N,
-                                                    int H, int W, int C, int c0, int cc,
-                                                    float thr, int nTx, int nT,
-                                                    float *__restrict__ sums, const WsHeader *hdr) {
+template <int CP, int UW, int UX, int UY>
+__global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward(
+    const GRec *__restrict__ recs, const float *__restrict__ params,
+    const float *__restrict__ gimg, const int *__restrict__ tile_off,
+    const int *__restrict__ list, int B, int N, int H, int W, int C, int c0, int cc, float thr,
+    int nTx, int nT, float *__restrict__ sums, const WsHeader *hdr) {
+  using WL = WaveLayout<UW, UX, UY>;
+  constexpr int UH = WL::kUH;
   constexpr int K = CP + 5;
   constexpr int KP = Pow2Up<K>::value;
   int f, t;
   if (!xcd_frame_item(blockIdx.x, nT, B, &f, &t)) return;
   if (hdr->status & (kStatusOverflow | kStatusStale)) return;
-  __shared__ BatchLds<CP> s;
-  const int lane = threadIdx.x;
-  const int tx = t % nTx, ty = t / nTx;
-  const int px = tx * kTile + (lane & 15);
-  const int py0 = ty * kTile + (lane >> 4);
-  const int ystrip0 = ty * kTile;
-  const float fx = (float)px + 0.5f, fy = (float)py0 + 0.5f;
+  __shared__ BatchLds<CP, WL::kBatch> s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
+  const int tx0 = (t % nTx) * kTile, ty0 = (t / nTx) * kTile;
+  const int rx0 = tx0, ry0 = ty0 + wave * WL::kRH;
+  const int mshift = wave * WL::kUnitsPerWave;
+  const int lx = lane % UW, ly = lane / UW;
+  const float fx = (float)(rx0 + lx) + 0.5f, fy = (float)(ry0 + ly) + 0.5f;
   const int P = 5 + C;
   const size_t gbase = (size_t)f * N;
 
-  float G[4][CP];
+  float G[UY][UX][CP];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int py = py0 + 4 * k;
-    const bool in = px < W && py < H;
-    const float *g = gimg + (((size_t)f * H + (in ? py : 0)) * W + (in ? px : 0)) * (size_t)C + c0;
+  for (int j = 0; j < UY; ++j) {
 #pragma unroll
-    for (int c = 0; c < CP; ++c) G[k][c] = (in && c < cc) ? g[c] : 0.f;
+    for (int i = 0; i < UX; ++i) {
+      const int px = rx0 + UW * i + lx, py = ry0 + UH * j + ly;
+      const bool in = px < W && py < H;
+      const float *g =
+          gimg + (((size_t)f * H + (in ? py : 0)) * W + (in ? px : 0)) * (size_t)C + c0;
+#pragma unroll
+      for (int c = 0; c < CP; ++c) G[j][i][c] = (in && c < cc) ? g[c] : 0.f;
+    }
   }
   const int vidx = value_index<KP>(lane & (KP - 1));
   int slot = -1;
@@ -205,51 +251,59 @@ __global__ __launch_bounds__(kWave) void k_backward(const GRec *__restrict__ rec
   }
 
   const int beg = tile_off[(size_t)f * nT + t], end = tile_off[(size_t)f * nT + t + 1];
-  for (int s0 = beg; s0 < end; s0 += kWave) {
-    const int cnt = min(kWave, end - s0);
+  for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
+    const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
-    stage_batch<CP>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, lane);
+    stage_batch<CP, WL::kBatch, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0,
+                                    ty0);
     __syncthreads();
-    for (int j = 0; j < cnt; ++j) {
-      const GRec r = s.rec[j];
-      int k0, k1;
-      strip_range(__builtin_amdgcn_readfirstlane(r.by), ystrip0, &k0, &k1);
+    for (int e = 0; e < cnt; ++e) {
+      const unsigned int um =
+          (__builtin_amdgcn_readfirstlane(s.mask[e]) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+      if (um == 0u) continue;
+      const GRec r = s.rec[e];
       const float dx = fx - r.mx, dy = fy - r.my;
       const float z1 = r.l11 * dx + r.l12 * dy;
       const float z2 = r.l21 * dx + r.l22 * dy;
-      const float st1 = 4.f * r.l12, st2 = 4.f * r.l22;
       float a[CP];
 #pragma unroll
-      for (int c = 0; c < CP; ++c) a[c] = s.amp[j][c];
+      for (int c = 0; c < CP; ++c) a[c] = s.amp[e][c];
       float part[KP];
 #pragma unroll
-      for (int i = 0; i < KP; ++i) part[i] = 0.f;
+      for (int k = 0; k < KP; ++k) part[k] = 0.f;
       bool any = false;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (k < k0 || k > k1) continue;
-        const float u1 = z1 + (float)k * st1;
-        const float u2 = z2 + (float)k * st2;
-        const float q = u1 * u1 + u2 * u2;
-        const bool inside = q <= thr;
-        any = any || inside;
-        const float w = inside ? __builtin_amdgcn_exp2f(-q) : 0.f;
-        float h = 0.f;
+      for (int j = 0; j < UY; ++j) {
+        if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
+        const float zr1 = j ? fmaf((float)(UH * j), r.l12, z1) : z1;
+        const float zr2 = j ? fmaf((float)(UH * j), r.l22, z2) : z2;
 #pragma unroll
-        for (int c = 0; c < CP; ++c) h += G[k][c] * a[c];
-        const float v = h * w;
+        for (int i = 0; i < UX; ++i) {
+          if (!(um & (1u << (j * UX + i)))) continue;
+          const float u1 = i ? fmaf((float)(UW * i), r.l11, zr1) : zr1;
+          const float u2 = i ? fmaf((float)(UW * i), r.l21, zr2) : zr2;
+          const float q = u1 * u1 + u2 * u2;
+          const bool inside = q <= thr;
+          if (__builtin_amdgcn_ballot_w64(inside) == 0ull) continue;
+          any = true;
+          const float w = inside ? __builtin_amdgcn_exp2f(-q) : 0.f;
+          float h = 0.f;
 #pragma unroll
-        for (int c = 0; c < CP; ++c) part[c] += G[k][c] * w;
-        const float t1 = v * u1, t2 = v * u2;
-        part[CP + 0] += t1;
-        part[CP + 1] += t2;
-        part[CP + 2] += t1 * u1;
-        part[CP + 3] += t2 * u2;
-        part[CP + 4] += t1 * u2;
+          for (int c = 0; c < CP; ++c) h += G[j][i][c] * a[c];
+          const float v = h * w;
+#pragma unroll
+          for (int c = 0; c < CP; ++c) part[c] += G[j][i][c] * w;
+          const float t1 = v * u1, t2 = v * u2;
+          part[CP + 0] += t1;
+          part[CP + 1] += t2;
+          part[CP + 2] += t1 * u1;
+          part[CP + 3] += t2 * u2;
+          part[CP + 4] += t1 * u2;
+        }
       }
-      if (__builtin_amdgcn_ballot_w64(any) == 0ull) continue;
+      if (!any) continue;
       const float tot = wave_reduce_transposed<KP>(part, lane);
-      if (slot >= 0) unsafeAtomicAdd(sums + (gbase + s.idx[j]) * (size_t)P + slot, tot);
+      if (slot >= 0) unsafeAtomicAdd(sums + (size_t)s.gidx[e] * P + slot, tot);
     }
   }
 }
@@ -313,57 +367,102 @@ __global__ __launch_bounds__(256) void k_zero_verify(float *__restrict__ p, long
 // ----------------------------------------------------------------------------
 // host launchers
 
-static int channel_pad(int cc) {
-  if (cc <= 4) return cc;
-  if (cc <= 8) return 8;
-  return 16;
-}
+namespace {
 
-template <int CP>
-static void launch_fwd_cp(dim3 grid, hipStream_t st, const GRec *recs, const float *params,
-                          const int *tile_off, const int *list, int B, int N, int H, int W, int C,
-                          int c0, int cc, float thr, int nTx, int nT, float *image,
-                          const WsHeader *hdr) {
+struct RasterArgs {
+  const GRec *recs;
+  const float *params;
+  const float *gimg;
+  const int *tile_off;
+  const int *list;
+  int B, N, H, W, C, c0, cc;
+  float thr;
+  int nTx, nT;
+  float *out;
+  const WsHeader *hdr;
+};
+
+template <int CP, int UW, int UX, int UY>
+void fwd_cp(const RasterArgs &a, hipStream_t st) {
+  using WL = WaveLayout<UW, UX, UY>;
+  dim3 grid((unsigned)xcd_grid(a.nT, a.B));
   PDR_TIMED(PDR_K_FORWARD_RASTER, st,
-            hipLaunchKernelGGL(k_forward<CP>, grid, dim3(kWave), 0, st, recs, params, tile_off,
-                               list, B, N, H, W, C, c0, cc, thr, nTx, nT, image, hdr));
+            hipLaunchKernelGGL((k_forward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
+                               a.recs, a.params, a.tile_off, a.list, a.B, a.N, a.H, a.W, a.C,
+                               a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.hdr));
 }
 
-template <int CP>
-static void launch_bwd_cp(dim3 grid, hipStream_t st, const GRec *recs, const float *params,
-                          const float *gimg, const int *tile_off, const int *list, int B, int N,
-                          int H, int W, int C, int c0, int cc, float thr, int nTx, int nT,
-                          float *sums, const WsHeader *hdr) {
+template <int CP, int UW, int UX, int UY>
+void bwd_cp(const RasterArgs &a, hipStream_t st) {
+  using WL = WaveLayout<UW, UX, UY>;
+  dim3 grid((unsigned)xcd_grid(a.nT, a.B));
   PDR_TIMED(PDR_K_BACKWARD_RASTER, st,
-            hipLaunchKernelGGL(k_backward<CP>, grid, dim3(kWave), 0, st, recs, params, gimg,
-                               tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, sums, hdr));
+            hipLaunchKernelGGL((k_backward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
+                               a.recs, a.params, a.gimg, a.tile_off, a.list, a.B, a.N, a.H, a.W,
+                               a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.hdr));
 }
 
-static float threshold(float radius) {
+// Unit shape and units per wave (compile-time tuning knob): 8x8 quads,
+// 2x2 per wave, one wave per tile (measured faster than 16x4 strips and
+// than two or four waves per tile).  A wave always spans the tile's width.
+#ifndef PDR_UNIT_W
+#define PDR_UNIT_W 8
+#define PDR_UNITS_X 2
+#define PDR_UNITS_Y 2
+#endif
+template <bool BWD>
+void dispatch(const RasterArgs &a, hipStream_t st) {
+  constexpr int UW = PDR_UNIT_W, UX = PDR_UNITS_X, UY = PDR_UNITS_Y;
+  const int cc = a.cc;
+  if (cc <= 1) {
+    BWD ? bwd_cp<1, UW, UX, UY>(a, st) : fwd_cp<1, UW, UX, UY>(a, st);
+  } else if (cc == 2) {
+    BWD ? bwd_cp<2, UW, UX, UY>(a, st) : fwd_cp<2, UW, UX, UY>(a, st);
+  } else if (cc == 3) {
+    BWD ? bwd_cp<3, UW, UX, UY>(a, st) : fwd_cp<3, UW, UX, UY>(a, st);
+  } else if (cc == 4) {
+    BWD ? bwd_cp<4, UW, UX, UY>(a, st) : fwd_cp<4, UW, UX, UY>(a, st);
+  } else if (cc <= 8) {
+    BWD ? bwd_cp<8, UW, UX, UY>(a, st) : fwd_cp<8, UW, UX, UY>(a, st);
+  } else {
+    BWD ? bwd_cp<16, UW, UX, UY>(a, st) : fwd_cp<16, UW, UX, UY>(a, st);
+  }
+}
+
+float threshold(float radius) {
   // q' <= k^2 log2(e)/2, rounded once to fp32
   return (float)((double)radius * (double)radius * kKappa2);
 }
 
+RasterArgs raster_args(const float *params, int B, int N, int H, int W, int C, float radius,
+                       void *ws, const Layout &L) {
+  char *w = (char *)ws;
+  RasterArgs a;
+  a.recs = (const GRec *)(w + L.recs);
+  a.params = params;
+  a.gimg = nullptr;
+  a.tile_off = (const int *)(w + L.tile_off);
+  a.list = (const int *)(w + L.list);
+  a.B = B; a.N = N; a.H = H; a.W = W; a.C = C;
+  a.c0 = 0; a.cc = C;
+  a.thr = threshold(radius);
+  a.nTx = (W + kTile - 1) / kTile;
+  a.nT = a.nTx * ((H + kTile - 1) / kTile);
+  a.out = nullptr;
+  a.hdr = (const WsHeader *)(w + L.hdr);
+  return a;
+}
+
+}  // namespace
+
 hipError_t launch_forward_raster(const float *params, float *image, int B, int N, int H, int W,
                                  int C, float radius, void *ws, const Layout &L, hipStream_t st) {
-  char *w = (char *)ws;
-  const WsHeader *hdr = (const WsHeader *)(w + L.hdr);
-  const GRec *recs = (const GRec *)(w + L.recs);
-  const int *tile_off = (const int *)(w + L.tile_off);
-  const int *list = (const int *)(w + L.list);
-  int nTx = (W + kTile - 1) / kTile, nTy = (H + kTile - 1) / kTile, nT = nTx * nTy;
-  dim3 grid((unsigned)xcd_grid(nT, B));
-  float thr = threshold(radius);
+  RasterArgs a = raster_args(params, B, N, H, W, C, radius, ws, L);
+  a.out = image;
   for (int c0 = 0; c0 < C; c0 += 16) {
-    int cc = C - c0 < 16 ? C - c0 : 16;
-    switch (channel_pad(cc)) {
-      case 1: launch_fwd_cp<1>(grid, st, recs, params, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, image, hdr); break;
-      case 2: launch_fwd_cp<2>(grid, st, recs, params, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, image, hdr); break;
-      case 3: launch_fwd_cp<3>(grid, st, recs, params, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, image, hdr); break;
-      case 4: launch_fwd_cp<4>(grid, st, recs, params, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, image, hdr); break;
-      case 8: launch_fwd_cp<8>(grid, st, recs, params, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, image, hdr); break;
-      default: launch_fwd_cp<16>(grid, st, recs, params, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, image, hdr); break;
-    }
+    a.c0 = c0;
+    a.cc = C - c0 < 16 ? C - c0 : 16;
+    dispatch<false>(a, st);
   }
   return hipGetLastError();
 }
@@ -371,12 +470,8 @@ hipError_t launch_forward_raster(const float *params, float *image, int B, int N
 hipError_t launch_backward(const float *params, const float *grad_image, float *grad_params, int B,
                            int N, int H, int W, int C, float radius, void *ws, const Layout &L,
                            bool check_stamp, hipStream_t st) {
-  char *w = (char *)ws;
-  WsHeader *hdr = (WsHeader *)(w + L.hdr);
-  const GRec *recs = (const GRec *)(w + L.recs);
-  const int *tile_off = (const int *)(w + L.tile_off);
-  const int *list = (const int *)(w + L.list);
-  int nTx = (W + kTile - 1) / kTile, nTy = (H + kTile - 1) / kTile, nT = nTx * nTy;
+  RasterArgs a = raster_args(params, B, N, H, W, C, radius, ws, L);
+  WsHeader *hdr = (WsHeader *)((char *)ws + L.hdr);
   long long BN = (long long)B * N, total = BN * (5 + C);
   long long zb = (total + 255) / 256;
   if (zb > 8192) zb = 8192;
@@ -384,18 +479,12 @@ hipError_t launch_backward(const float *params, const float *grad_image, float *
             hipLaunchKernelGGL(k_zero_verify, dim3((unsigned)zb), dim3(256), 0, st, grad_params,
                                total, hdr, check_stamp ? 1 : 0, B, N, H, W, C, radius,
                                (unsigned long long)(uintptr_t)params));
-  dim3 grid((unsigned)xcd_grid(nT, B));
-  float thr = threshold(radius);
+  a.gimg = grad_image;
+  a.out = grad_params;
   for (int c0 = 0; c0 < C; c0 += 16) {
-    int cc = C - c0 < 16 ? C - c0 : 16;
-    switch (channel_pad(cc)) {
-      case 1: launch_bwd_cp<1>(grid, st, recs, params, grad_image, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, grad_params, hdr); break;
-      case 2: launch_bwd_cp<2>(grid, st, recs, params, grad_image, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, grad_params, hdr); break;
-      case 3: launch_bwd_cp<3>(grid, st, recs, params, grad_image, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, grad_params, hdr); break;
-      case 4: launch_bwd_cp<4>(grid, st, recs, params, grad_image, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, grad_params, hdr); break;
-      case 8: launch_bwd_cp<8>(grid, st, recs, params, grad_image, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, grad_params, hdr); break;
-      default: launch_bwd_cp<16>(grid, st, recs, params, grad_image, tile_off, list, B, N, H, W, C, c0, cc, thr, nTx, nT, grad_params, hdr); break;
-    }
+    a.c0 = c0;
+    a.cc = C - c0 < 16 ? C - c0 : 16;
+    dispatch<true>(a, st);
   }
   PDR_TIMED(PDR_K_FINALIZE, st,
             hipLaunchKernelGGL(k_finalize, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,

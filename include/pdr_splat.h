@@ -61,13 +61,14 @@ int pdr_splat_tile_size(void);
 
 /* Bytes of workspace for a problem and a (tile, Gaussian) pair capacity.
  * Returns a negative pdr_status on invalid sizes.  The fixed part covers a
- * 256-byte header, 40 bytes per Gaussian and 8 bytes per tile; every pair
- * takes 4 more bytes.  max_pairs <= 2^31 - 1. */
+ * 256-byte header, 40 bytes per Gaussian, 8 bytes per tile and 4 bytes per
+ * tile row (each region rounded up to 256 bytes); every pair takes 4 more
+ * bytes.  max_pairs <= 2^31 - 1. */
 long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long max_pairs);
 
 /* Forward.  params [B][N][5+C] fp32 -> image [B][H][W][C] fp32 (overwritten).
  * Bins the Gaussians into the workspace (kept for a later backward with
- * reuse_binning = 1).  H, W <= 32767; B*N and B*H*W*C < 2^31. */
+ * reuse_binning = 1).  H <= 32767, W <= 16384, N <= 2^22, B*N < 2^31. */
 int pdr_splat_forward(const float *params, float *image, int B, int N, int H, int W, int C,
                       float radius, void *workspace, size_t workspace_bytes, void *stream);
 
@@ -105,7 +106,9 @@ const char *pdr_splat_status_string(int status);
  * pdr_splat_timing returns the previous state.  pdr_splat_timing_read waits
  * for the recorded events and fills total_ms[k] / launches[k] (arrays of
  * PDR_KERNEL_COUNT, may be NULL) with the accumulated milliseconds and launch
- * counts per kernel class k; reset != 0 clears the accumulators. */
+ * counts per kernel class k; reset != 0 clears the accumulators.  The
+ * scan of the per-tile counts runs inside the list-writing kernel, so
+ * PDR_K_SCAN records no launches. */
 enum pdr_kernel_id {
     PDR_K_PREPROCESS = 0, PDR_K_BIN_COUNT = 1, PDR_K_SCAN = 2, PDR_K_BIN_WRITE = 3,
     PDR_K_FORWARD_RASTER = 4, PDR_K_ZERO = 5, PDR_K_BACKWARD_RASTER = 6, PDR_K_FINALIZE = 7,

@@ -79,9 +79,14 @@ def check_against_oracle(orc, params, grad_image, H, W, radius=3.0, frames=None,
     return out
 
 
+def tile_size():
+    from differentiable_gaussian_splatting_pdr_amd import _lib
+    return _lib.pdr_splat_tile_size()
+
+
 def check_lists(orc, params, H, W, radius=3.0, gpu=None):
     off_g, lst_g = gpu if gpu is not None else gpu_bin(params, H, W, radius)
-    counts, off, lst, _ = orc.bin(params, H, W, radius)
+    counts, off, lst, _ = orc.bin(params, H, W, radius, tile=tile_size())
     assert np.array_equal(off_g, off), "tile offsets differ"
     assert np.array_equal(lst_g, lst), "tile lists differ"
     return int(off[-1])

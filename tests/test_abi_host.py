@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_tile_size_and_status_strings():
-    assert _lib.pdr_splat_tile_size() == 16
+    assert _lib.pdr_splat_tile_size() in (16, 32)
     for code in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(code) != "unknown status"
     assert _lib.status_string(-99) == "unknown status"
@@ -48,13 +48,17 @@ def test_workspace_bytes_layout():
     def a(v):
         return (v + 255) // 256 * 256
     B, N, H, W, C = 384, 4096, 128, 128, 3
-    bt = B * 64
-    fixed = a(256) + a(B * N * 32) + a(B * N * 8) + a(bt * 4) + a((bt + 1) * 4)
+    t = _lib.pdr_splat_tile_size()
+    bt = B * (128 // t) ** 2
+    rows = B * (128 // t)
+    fixed = a(256) + a(B * N * 32) + a(B * N * 8) + a(bt * 4) + a(rows * 4) + a((bt + 1) * 4)
     assert _lib.pdr_splat_workspace_bytes(B, N, H, W, C, 0) == fixed
     assert _lib.pdr_splat_workspace_bytes(B, N, H, W, C, 1000) == fixed + a(4000)
     # ragged sizes round the tile grid up
-    assert _lib.pdr_splat_workspace_bytes(1, 10, 17, 33, 1, 0) == (
-        a(256) + a(320) + a(80) + a(3 * 2 * 4) + a(7 * 4))
+    t = _lib.pdr_splat_tile_size()
+    nt = ((17 + t - 1) // t) * ((65 + t - 1) // t)
+    assert _lib.pdr_splat_workspace_bytes(1, 10, 17, 65, 1, 0) == (
+        a(256) + a(320) + a(80) + a(nt * 4) + a(((17 + t - 1) // t) * 4) + a((nt + 1) * 4))
 
 
 @pytest.mark.parametrize("args", [
@@ -79,7 +83,7 @@ def _fwd(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(params=None), -1), (dict(image=None), -1), (dict(B=0), -1), (dict(N=-3), -1),
-    (dict(C=0), -1), (dict(W=40000), -1), (dict(radius=0.0), -1), (dict(radius=-1.0), -1),
+    (dict(C=0), -1), (dict(W=40000), -1), (dict(W=16400), -1), (dict(radius=0.0), -1), (dict(radius=-1.0), -1),
     (dict(radius=math.nan), -1), (dict(radius=math.inf), -1), (dict(workspace=None), -1),
     (dict(workspace=FAKE + 4), -2), (dict(workspace_bytes=100), -2),
 ])

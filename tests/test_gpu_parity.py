@@ -136,7 +136,7 @@ def test_overflow_then_regrow(orc):
                            ws.ptr, ws.nbytes, st)
     rc, need = _lib.pdr_splat_check(ws.ptr, st)
     assert rc == _lib.PDR_ERR_OVERFLOW
-    _, off, _, _ = orc.bin(p, wl.H, wl.W)
+    _, off, _, _ = orc.bin(p, wl.H, wl.W, tile=_lib.pdr_splat_tile_size())
     assert need == off[-1]
     image, _ = splat.forward(pt, wl.H, wl.W, 3.0, workspace=ws)
     ref, slk, _, _ = orc.render(p, wl.H, wl.W)
@@ -184,4 +184,5 @@ def test_timing_counts_launches():
     finally:
         _lib.pdr_splat_timing(False)
     assert t["forward_raster"][1] == 1 and t["backward_raster"][1] == 1
+    assert t["bin_count"][1] == 1 and t["bin_write"][1] == 1 and t["scan"][1] == 0
     assert t["backward_raster"][0] > 0.0
