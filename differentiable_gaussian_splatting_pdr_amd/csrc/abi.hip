@@ -22,7 +22,7 @@ int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
   if (H > kMaxHW || W > kMaxHW || N > kMaxN) return PDR_ERR_INVALID_ARG;
   if ((W + kTile - 1) / kTile > kMaxGroupTiles) return PDR_ERR_INVALID_ARG;  // one tile row per bin group
   long long BN = (long long)B * N;
-  if (BN > 0x7fffffffLL || BN * (5 + C) > 0x7fffffffffffLL) return PDR_ERR_INVALID_ARG;
+  if (BN * (5 + C) > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;  // int32 parameter offsets
   if ((long long)B * H * W * C > (1LL << 46)) return PDR_ERR_INVALID_ARG;
   d->nTx = (W + kTile - 1) / kTile;
   d->nTy = (H + kTile - 1) / kTile;

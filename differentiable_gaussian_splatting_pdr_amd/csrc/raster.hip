@@ -43,19 +43,26 @@ struct WaveLayout {
   static constexpr int kBatch = kThreads;  // list entries staged per round
 };
 
-template <int CP, int NB>
-struct BatchLds {
-  GRec rec[NB];
-  float amp[NB][CP];
-  unsigned int mask[NB];  // tile units (row-major) the Gaussian's pixel box meets
-  int gidx[NB];           // frame * N + n
+// One staged list entry (interleaved so that a wave reads it from one LDS
+// base address): the whitening rows, the mean relative to the tile origin
+// (so that p - mu is formed from small tile-local numbers: exact for pixels
+// near the mean; folding mu into an offset c = -L mu instead cancels
+// catastrophically for tiny Gaussians, whose L is large), the mask of tile
+// units the pixel box meets, the element offset of the Gaussian's parameter
+// row, and its amplitudes.
+template <int CP>
+struct alignas(16) Entry {
+  float l11, l12, l21, l22;
+  float mx, my;
+  unsigned int mask;
+  int row;  // (frame * N + n) * (5 + C)
+  float amp[(CP + 3) / 4 * 4];
 };
 
-// One list entry per thread of the workgroup: record, amplitudes, and the
-// mask of tile units its pixel box meets (computed here, in parallel, so
-// the per-entry loop only tests bits).
-template <int CP, int NB, int UW>
-__device__ __forceinline__ void stage_batch(BatchLds<CP, NB> &s, const GRec *__restrict__ recs,
+// One list entry per thread of the workgroup (computed here, in parallel,
+// so that the per-entry loop only reads and tests bits).
+template <int CP, int UW>
+__device__ __forceinline__ void stage_entry(Entry<CP> *s, const GRec *__restrict__ recs,
                                             const float *__restrict__ params,
                                             const int *__restrict__ list, int s0, int cnt,
                                             size_t gbase, int P, int c0, int cc, int tid,
@@ -64,22 +71,29 @@ __device__ __forceinline__ void stage_batch(BatchLds<CP, NB> &s, const GRec *__r
   if (tid < cnt) {
     const int n = list[s0 + tid];
     const GRec r = recs[gbase + n];
-    s.gidx[tid] = (int)gbase + n;
-    s.rec[tid] = r;
-    const float *a = params + (gbase + n) * (size_t)P + 5 + c0;
+    Entry<CP> e;
+    e.l11 = r.l11;
+    e.l12 = r.l12;
+    e.l21 = r.l21;
+    e.l22 = r.l22;
+    e.mx = r.mx - (float)tx0;
+    e.my = r.my - (float)ty0;
+    e.row = ((int)gbase + n) * P;
+    const float *a = params + (size_t)e.row + 5 + c0;
 #pragma unroll
-    for (int c = 0; c < CP; ++c) s.amp[tid][c] = c < cc ? a[c] : 0.f;
+    for (int c = 0; c < (CP + 3) / 4 * 4; ++c) e.amp[c] = c < cc ? a[c] : 0.f;
     // listed => the box meets the tile; clamp it to the tile's units
     const int ux0 = max(0, ((int)(r.bx & 0xffffu) - tx0) / UW);
     const int ux1 = min(NUX - 1, ((int)(r.bx >> 16) - tx0) / UW);
     const int uy0 = max(0, ((int)(r.by & 0xffffu) - ty0) / UH);
     const int uy1 = min(NUY - 1, ((int)(r.by >> 16) - ty0) / UH);
-    const unsigned int row = ((2u << ux1) - 1u) & ~((1u << ux0) - 1u);
+    const unsigned int rowm = ((2u << ux1) - 1u) & ~((1u << ux0) - 1u);
     unsigned int m = 0u;
 #pragma unroll
     for (int j = 0; j < NUY; ++j)
-      if (j >= uy0 && j <= uy1) m |= row << (j * NUX);
-    s.mask[tid] = m;
+      if (j >= uy0 && j <= uy1) m |= rowm << (j * NUX);
+    e.mask = m;
+    s[tid] = e;
   }
 }
 
@@ -94,14 +108,15 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
   int f, t;
   if (!xcd_frame_item(blockIdx.x, nT, B, &f, &t)) return;
   if (hdr->status & kStatusOverflow) return;
-  __shared__ BatchLds<CP, WL::kBatch> s;
+  __shared__ Entry<CP> s[WL::kBatch];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int tx0 = (t % nTx) * kTile, ty0 = (t / nTx) * kTile;
   const int rx0 = tx0, ry0 = ty0 + wave * WL::kRH;
   const int mshift = wave * WL::kUnitsPerWave;
   const int lx = lane % UW, ly = lane / UW;
-  const float fx = (float)(rx0 + lx) + 0.5f, fy = (float)(ry0 + ly) + 0.5f;
+  // tile-local pixel centre of the lane in its first unit
+  const float fx = (float)(rx0 - tx0 + lx) + 0.5f, fy = (float)(ry0 - ty0 + ly) + 0.5f;
   const int P = 5 + C;
   const size_t gbase = (size_t)f * N;
   float acc[UY][UX][CP];
@@ -112,24 +127,24 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
 #pragma unroll
       for (int c = 0; c < CP; ++c) acc[j][i][c] = 0.f;
 
-  const int beg = tile_off[(size_t)f * nT + t], end = tile_off[(size_t)f * nT + t + 1];
+  const int beg = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t]);
+  const int end = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t + 1]);
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
-    stage_batch<CP, WL::kBatch, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0,
-                                    ty0);
+    stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0);
     __syncthreads();
     for (int e = 0; e < cnt; ++e) {
       const unsigned int um =
-          (__builtin_amdgcn_readfirstlane(s.mask[e]) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+          (__builtin_amdgcn_readfirstlane(s[e].mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
       if (um == 0u) continue;
-      const GRec r = s.rec[e];
+      const Entry<CP> r = s[e];
       const float dx = fx - r.mx, dy = fy - r.my;
       const float z1 = r.l11 * dx + r.l12 * dy;
       const float z2 = r.l21 * dx + r.l22 * dy;
       float a[CP];
 #pragma unroll
-      for (int c = 0; c < CP; ++c) a[c] = s.amp[e][c];
+      for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
 #pragma unroll
       for (int j = 0; j < UY; ++j) {
         if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
@@ -219,14 +234,15 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
   int f, t;
   if (!xcd_frame_item(blockIdx.x, nT, B, &f, &t)) return;
   if (hdr->status & (kStatusOverflow | kStatusStale)) return;
-  __shared__ BatchLds<CP, WL::kBatch> s;
+  __shared__ Entry<CP> s[WL::kBatch];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int tx0 = (t % nTx) * kTile, ty0 = (t / nTx) * kTile;
   const int rx0 = tx0, ry0 = ty0 + wave * WL::kRH;
   const int mshift = wave * WL::kUnitsPerWave;
   const int lx = lane % UW, ly = lane / UW;
-  const float fx = (float)(rx0 + lx) + 0.5f, fy = (float)(ry0 + ly) + 0.5f;
+  // tile-local pixel centre of the lane in its first unit
+  const float fx = (float)(rx0 - tx0 + lx) + 0.5f, fy = (float)(ry0 - ty0 + ly) + 0.5f;
   const int P = 5 + C;
   const size_t gbase = (size_t)f * N;
 
@@ -250,24 +266,24 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
     else if (vidx < K) slot = vidx - CP;
   }
 
-  const int beg = tile_off[(size_t)f * nT + t], end = tile_off[(size_t)f * nT + t + 1];
+  const int beg = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t]);
+  const int end = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t + 1]);
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
-    stage_batch<CP, WL::kBatch, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0,
-                                    ty0);
+    stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0);
     __syncthreads();
     for (int e = 0; e < cnt; ++e) {
       const unsigned int um =
-          (__builtin_amdgcn_readfirstlane(s.mask[e]) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+          (__builtin_amdgcn_readfirstlane(s[e].mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
       if (um == 0u) continue;
-      const GRec r = s.rec[e];
+      const Entry<CP> r = s[e];
       const float dx = fx - r.mx, dy = fy - r.my;
       const float z1 = r.l11 * dx + r.l12 * dy;
       const float z2 = r.l21 * dx + r.l22 * dy;
       float a[CP];
 #pragma unroll
-      for (int c = 0; c < CP; ++c) a[c] = s.amp[e][c];
+      for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
       float part[KP];
 #pragma unroll
       for (int k = 0; k < KP; ++k) part[k] = 0.f;
@@ -303,7 +319,7 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
       }
       if (!any) continue;
       const float tot = wave_reduce_transposed<KP>(part, lane);
-      if (slot >= 0) unsafeAtomicAdd(sums + (size_t)s.gidx[e] * P + slot, tot);
+      if (slot >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot), tot);
     }
   }
 }

@@ -68,7 +68,7 @@ long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long
 
 /* Forward.  params [B][N][5+C] fp32 -> image [B][H][W][C] fp32 (overwritten).
  * Bins the Gaussians into the workspace (kept for a later backward with
- * reuse_binning = 1).  H <= 32767, W <= 16384, N <= 2^22, B*N < 2^31. */
+ * reuse_binning = 1).  H <= 32767, W <= 16384, N <= 2^22, B*N*(5+C) < 2^31. */
 int pdr_splat_forward(const float *params, float *image, int B, int N, int H, int W, int C,
                       float radius, void *workspace, size_t workspace_bytes, void *stream);
 

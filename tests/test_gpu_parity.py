@@ -78,6 +78,20 @@ def test_edge_cases(orc):
     assert np.all(np.isfinite(res["image"]))
 
 
+def test_tiny_gaussians(orc):
+    # |L| ~ 1/s is large: p - mu must be formed without cancellation (means on
+    # and near pixel centres, in several tiles)
+    rng = np.random.default_rng(21)
+    B, N, H, W, C = 1, 60, 70, 70, 2
+    p, g = workloads.make_custom(B, N, H, W, C, seed=21)
+    p[0, :, 0] = rng.integers(0, W, N) + 0.5 + rng.choice([0.0, 1e-3, -0.25], N)
+    p[0, :, 1] = rng.integers(0, H, N) + 0.5 + rng.choice([0.0, 2e-3, 0.4], N)
+    p[0, :, 2] = np.exp(rng.uniform(np.log(1e-3), np.log(0.4), N))
+    p[0, :, 3] = np.exp(rng.uniform(np.log(1e-3), np.log(0.4), N))
+    check_lists(orc, p, H, W)
+    check_against_oracle(orc, p, g, H, W)
+
+
 def test_single_gaussian_closed_form():
     # GPU vs the closed form a 2 pi s1 s2 of an untruncated Gaussian (fp32)
     H = W = 96
