@@ -20,12 +20,12 @@ struct Dims {
 int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
   if (B < 1 || N < 1 || H < 1 || W < 1 || C < 1) return PDR_ERR_INVALID_ARG;
   if (H > kMaxHW || W > kMaxHW || N > kMaxN) return PDR_ERR_INVALID_ARG;
-  if ((W + kTile - 1) / kTile > kMaxGroupTiles) return PDR_ERR_INVALID_ARG;  // one tile row per bin group
+  if ((W + kTileW - 1) / kTileW > kMaxGroupTiles) return PDR_ERR_INVALID_ARG;  // one tile row per bin group
   long long BN = (long long)B * N;
   if (BN * (5 + C) > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;  // int32 parameter offsets
   if ((long long)B * H * W * C > (1LL << 46)) return PDR_ERR_INVALID_ARG;
-  d->nTx = (W + kTile - 1) / kTile;
-  d->nTy = (H + kTile - 1) / kTile;
+  d->nTx = (W + kTileW - 1) / kTileW;
+  d->nTy = (H + kTileH - 1) / kTileH;
   d->BN = BN;
   d->BT = (long long)B * d->nTx * d->nTy;
   d->BR = (long long)B * d->nTy;
@@ -57,7 +57,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PDR_OK : PDR_ERR_HIP; }
 
 extern "C" {
 
-int pdr_splat_tile_size(void) { return kTile; }
+int pdr_splat_tile_size(void) { return kTileW; }
 
 long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long max_pairs) {
   Dims d;

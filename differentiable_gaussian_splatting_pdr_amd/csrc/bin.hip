@@ -104,7 +104,7 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
   return t;
 }
 
-// LDS bit matrix binning.  Grid: (groups per frame G, frames B); a group is
+// LDS bit matrix binning.  Grid: G bands x B frames (1D, XCD-aware); a group is
 // a band of gh whole tile rows.  Dynamic LDS: Tg * (NC / 32) words, NC a
 // multiple of 64.
 //
@@ -126,7 +126,8 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
   __shared__ int base[kMaxGroupTiles];
   __shared__ long long red[kBinThreads / kWave];
   __shared__ int wtot[kBinThreads / kWave];
-  const int b = blockIdx.y, g = blockIdx.x;
+  int b, g;  // frame, band: all bands of a frame on one XCD, so its boxes stay in that L2
+  if (!xcd_frame_item(blockIdx.x, G, B, &b, &g)) return;
   const int ty0 = g * gh;
   const int ah = min(gh, nTy - ty0);
   const int Tg = nTx * ah;
@@ -185,8 +186,8 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
       int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
       int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
       if (x0 > x1) continue;
-      int ux0 = x0 >> kTileShift, ux1 = x1 >> kTileShift;
-      int uy0 = max(y0 >> kTileShift, ty0), uy1 = min(y1 >> kTileShift, ty0 + ah - 1);
+      int ux0 = x0 >> kTileShiftX, ux1 = x1 >> kTileShiftX;
+      int uy0 = max(y0 >> kTileShiftY, ty0), uy1 = min(y1 >> kTileShiftY, ty0 + ah - 1);
       const unsigned int bit = 1u << (i & 31);
       const int wi = i >> 5;
       for (int ty = uy0; ty <= uy1; ++ty)
@@ -265,7 +266,7 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   int *counts = (int *)(w + L.counts);
   int *gtot = (int *)(w + L.gtot);
   long long BN = (long long)B * N;
-  int nTx = (W + kTile - 1) / kTile, nTy = (H + kTile - 1) / kTile;
+  int nTx = (W + kTileW - 1) / kTileW, nTy = (H + kTileH - 1) / kTileH;
   PDR_TIMED(PDR_K_PREPROCESS, st,
             hipLaunchKernelGGL(k_preprocess, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,
                                params, (int)BN, C, H, W, radius, recs, boxes, hdr, N,
@@ -274,7 +275,7 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   choose_groups(B, N, nTx, nTy, &gh, &NC);
   int G = (nTy + gh - 1) / gh;
   size_t lds = (size_t)nTx * gh * (NC / 32) * 4;
-  dim3 grid((unsigned)G, (unsigned)B);
+  dim3 grid((unsigned)xcd_grid(G, B));
   PDR_TIMED(PDR_K_BIN_COUNT, st,
             hipLaunchKernelGGL(k_bin<false>, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx,
                                nTy, gh, G, NC, counts, gtot, (int *)nullptr, (int *)nullptr, cap,

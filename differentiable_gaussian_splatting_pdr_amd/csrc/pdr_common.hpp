@@ -7,8 +7,15 @@
 
 namespace pdr {
 
-constexpr int kTileShift = 4;
-constexpr int kTile = 1 << kTileShift;  // tile edge in pixels (binning and raster)
+// Tile shape in pixels (binning and raster); compile-time tuning knobs.
+#ifndef PDR_TILE_SHIFT_X
+#define PDR_TILE_SHIFT_X 4
+#endif
+#ifndef PDR_TILE_SHIFT_Y
+#define PDR_TILE_SHIFT_Y 4
+#endif
+constexpr int kTileShiftX = PDR_TILE_SHIFT_X, kTileShiftY = PDR_TILE_SHIFT_Y;
+constexpr int kTileW = 1 << kTileShiftX, kTileH = 1 << kTileShiftY;
 constexpr int kWave = 64;        // CDNA wavefront width
 constexpr int kBinThreads = 512; // binning workgroup
 constexpr int kMaxHW = 32767;    // pixel boxes are packed as 16-bit coordinates

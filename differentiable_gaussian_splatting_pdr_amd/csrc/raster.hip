@@ -13,9 +13,10 @@
 //
 // Per (Gaussian, pixel): z = L (p - mu) with L the whitening rows scaled by
 // sqrt(log2(e)/2), q' = z1^2 + z2^2, w = exp2(-q') if q' <= k^2 log2(e)/2.
-// This equals exp(-q/2) with the Mahalanobis q of the definition.  Moving
-// by whole units is linear: z(p + (i UW, j UH)) = z(p) + i UW L e_x +
-// j UH L e_y, evaluated with one fma per component.
+// This equals exp(-q/2) with the Mahalanobis q of the definition.  p - mu
+// is formed for every unit from exact tile-local coordinates (stepping z by
+// whole units instead, z + 8 L e_x, loses eps |L| 16 to cancellation, which
+// is visible for tiny Gaussians whose |L| ~ 1/s is large).
 //
 // Forward: C channel accumulators per pixel in registers.
 // Backward: per lane the partial sums over its pixels of
@@ -36,8 +37,8 @@ template <int UW, int UX, int UY>
 struct WaveLayout {
   static constexpr int kUH = kWave / UW;
   static constexpr int kRW = UX * UW, kRH = UY * kUH;  // wave region
-  static_assert(kRW == kTile && kTile % kRH == 0, "a wave spans the tile's width");
-  static constexpr int kWaves = kTile / kRH;
+  static_assert(kRW == kTileW && kTileH % kRH == 0, "a wave spans the tile's width");
+  static constexpr int kWaves = kTileH / kRH;
   static constexpr int kUnitsPerWave = UX * UY;  // consecutive bits of the tile's unit mask
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kBatch = kThreads;  // list entries staged per round
@@ -67,7 +68,7 @@ __device__ __forceinline__ void stage_entry(Entry<CP> *s, const GRec *__restrict
                                             const int *__restrict__ list, int s0, int cnt,
                                             size_t gbase, int P, int c0, int cc, int tid,
                                             int tx0, int ty0) {
-  constexpr int UH = kWave / UW, NUX = kTile / UW, NUY = kTile / UH;
+  constexpr int UH = kWave / UW, NUX = kTileW / UW, NUY = kTileH / UH;
   if (tid < cnt) {
     const int n = list[s0 + tid];
     const GRec r = recs[gbase + n];
@@ -111,7 +112,7 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
   __shared__ Entry<CP> s[WL::kBatch];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-  const int tx0 = (t % nTx) * kTile, ty0 = (t / nTx) * kTile;
+  const int tx0 = (t % nTx) * kTileW, ty0 = (t / nTx) * kTileH;
   const int rx0 = tx0, ry0 = ty0 + wave * WL::kRH;
   const int mshift = wave * WL::kUnitsPerWave;
   const int lx = lane % UW, ly = lane / UW;
@@ -139,22 +140,19 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
           (__builtin_amdgcn_readfirstlane(s[e].mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
       if (um == 0u) continue;
       const Entry<CP> r = s[e];
-      const float dx = fx - r.mx, dy = fy - r.my;
-      const float z1 = r.l11 * dx + r.l12 * dy;
-      const float z2 = r.l21 * dx + r.l22 * dy;
       float a[CP];
 #pragma unroll
       for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
 #pragma unroll
       for (int j = 0; j < UY; ++j) {
         if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
-        const float zr1 = j ? fmaf((float)(UH * j), r.l12, z1) : z1;
-        const float zr2 = j ? fmaf((float)(UH * j), r.l22, z2) : z2;
+        const float dy = (fy + (float)(UH * j)) - r.my;
 #pragma unroll
         for (int i = 0; i < UX; ++i) {
           if (!(um & (1u << (j * UX + i)))) continue;
-          const float u1 = i ? fmaf((float)(UW * i), r.l11, zr1) : zr1;
-          const float u2 = i ? fmaf((float)(UW * i), r.l21, zr2) : zr2;
+          const float dx = (fx + (float)(UW * i)) - r.mx;
+          const float u1 = r.l11 * dx + r.l12 * dy;
+          const float u2 = r.l21 * dx + r.l22 * dy;
           const float q = u1 * u1 + u2 * u2;
           const float w = q <= thr ? __builtin_amdgcn_exp2f(-q) : 0.f;
 #pragma unroll
@@ -237,7 +235,7 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
   __shared__ Entry<CP> s[WL::kBatch];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-  const int tx0 = (t % nTx) * kTile, ty0 = (t / nTx) * kTile;
+  const int tx0 = (t % nTx) * kTileW, ty0 = (t / nTx) * kTileH;
   const int rx0 = tx0, ry0 = ty0 + wave * WL::kRH;
   const int mshift = wave * WL::kUnitsPerWave;
   const int lx = lane % UW, ly = lane / UW;
@@ -278,9 +276,6 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
           (__builtin_amdgcn_readfirstlane(s[e].mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
       if (um == 0u) continue;
       const Entry<CP> r = s[e];
-      const float dx = fx - r.mx, dy = fy - r.my;
-      const float z1 = r.l11 * dx + r.l12 * dy;
-      const float z2 = r.l21 * dx + r.l22 * dy;
       float a[CP];
 #pragma unroll
       for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
@@ -291,13 +286,13 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
 #pragma unroll
       for (int j = 0; j < UY; ++j) {
         if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
-        const float zr1 = j ? fmaf((float)(UH * j), r.l12, z1) : z1;
-        const float zr2 = j ? fmaf((float)(UH * j), r.l22, z2) : z2;
+        const float dy = (fy + (float)(UH * j)) - r.my;
 #pragma unroll
         for (int i = 0; i < UX; ++i) {
           if (!(um & (1u << (j * UX + i)))) continue;
-          const float u1 = i ? fmaf((float)(UW * i), r.l11, zr1) : zr1;
-          const float u2 = i ? fmaf((float)(UW * i), r.l21, zr2) : zr2;
+          const float dx = (fx + (float)(UW * i)) - r.mx;
+          const float u1 = r.l11 * dx + r.l12 * dy;
+          const float u2 = r.l21 * dx + r.l22 * dy;
           const float q = u1 * u1 + u2 * u2;
           const bool inside = q <= thr;
           if (__builtin_amdgcn_ballot_w64(inside) == 0ull) continue;
@@ -462,8 +457,8 @@ RasterArgs raster_args(const float *params, int B, int N, int H, int W, int C, f
   a.B = B; a.N = N; a.H = H; a.W = W; a.C = C;
   a.c0 = 0; a.cc = C;
   a.thr = threshold(radius);
-  a.nTx = (W + kTile - 1) / kTile;
-  a.nT = a.nTx * ((H + kTile - 1) / kTile);
+  a.nTx = (W + kTileW - 1) / kTileW;
+  a.nT = a.nTx * ((H + kTileH - 1) / kTileH);
   a.out = nullptr;
   a.hdr = (const WsHeader *)(w + L.hdr);
   return a;
