@@ -31,9 +31,11 @@ EXPORTED = (
     "pdr_splat_timing",
     "pdr_splat_timing_read",
     "pdr_splat_kernel_name",
+    "pdr_loss_workspace_bytes",
+    "pdr_loss_l1_ssim",
 )
 
-KERNEL_COUNT = 8
+KERNEL_COUNT = 11
 
 
 class PdrError(RuntimeError):
@@ -74,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.pdr_splat_timing_read.restype = i
         L.pdr_splat_kernel_name.argtypes = [i]
         L.pdr_splat_kernel_name.restype = ctypes.c_char_p
+        L.pdr_loss_workspace_bytes.argtypes = [i, i, i, i]
+        L.pdr_loss_workspace_bytes.restype = ll
+        L.pdr_loss_l1_ssim.argtypes = [vp, vp, i, i, i, i, f, f, f, vp, vp, vp, sz, vp]
+        L.pdr_loss_l1_ssim.restype = i
         _lib = L
     return _lib
 
@@ -137,3 +143,14 @@ def pdr_splat_timing_read(reset: bool = True):
     cnt = (ctypes.c_longlong * KERNEL_COUNT)()
     _raise(lib().pdr_splat_timing_read(ms, cnt, int(bool(reset))), "pdr_splat_timing_read")
     return {pdr_splat_kernel_name(k): (ms[k], cnt[k]) for k in range(KERNEL_COUNT)}
+
+
+def pdr_loss_workspace_bytes(B, H, W, C) -> int:
+    return _raise(lib().pdr_loss_workspace_bytes(B, H, W, C), "pdr_loss_workspace_bytes")
+
+
+def pdr_loss_l1_ssim(image, target, B, H, W, C, lam, c1, c2, grad_image, loss, workspace,
+                     workspace_bytes, stream):
+    return _raise(lib().pdr_loss_l1_ssim(image, target, B, H, W, C, float(lam), float(c1),
+                                         float(c2), grad_image, loss, workspace, workspace_bytes,
+                                         stream), "pdr_loss_l1_ssim")

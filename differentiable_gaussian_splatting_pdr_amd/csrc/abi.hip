@@ -135,6 +135,26 @@ int pdr_splat_check(void *workspace, void *stream, long long *pairs_needed) {
   return PDR_OK;
 }
 
+long long pdr_loss_workspace_bytes(int B, int H, int W, int C) {
+  if (B < 1 || H < 1 || W < 1 || C < 1) return PDR_ERR_INVALID_ARG;
+  if ((long long)B * H * W * C > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
+  return (long long)loss_workspace_bytes(B, H, W, C);
+}
+
+int pdr_loss_l1_ssim(const float *image, const float *target, int B, int H, int W, int C,
+                     float lambda, float c1, float c2, float *grad_image, double *loss,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  if (!image || !target || !grad_image || !loss || !workspace) return PDR_ERR_INVALID_ARG;
+  long long need = pdr_loss_workspace_bytes(B, H, W, C);
+  if (need < 0) return (int)need;
+  if (!(lambda >= 0.f && lambda <= 1.f) || !(c1 > 0.f) || !(c2 > 0.f) || !isfinite(c1) ||
+      !isfinite(c2))
+    return PDR_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & 255u) != 0 || workspace_bytes < (size_t)need) return PDR_ERR_WORKSPACE;
+  return hip_status(launch_loss(image, target, B, H, W, C, lambda, c1, c2, grad_image, loss,
+                                workspace, (hipStream_t)stream));
+}
+
 const char *pdr_splat_status_string(int status) {
   switch (status) {
     case PDR_OK: return "ok";

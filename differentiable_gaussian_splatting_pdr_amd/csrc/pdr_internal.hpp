@@ -40,4 +40,9 @@ hipError_t launch_backward(const float *params, const float *grad_image, float *
                            int N, int H, int W, int C, float radius, void *ws, const Layout &L,
                            bool check_stamp, hipStream_t st);
 
+// L1 + SSIM loss: grad = dloss/dimage, *loss on the device.
+hipError_t launch_loss(const float *img, const float *tgt, int B, int H, int W, int C, float lam,
+                       float c1, float c2, float *grad, double *loss, void *ws, hipStream_t st);
+size_t loss_workspace_bytes(int B, int H, int W, int C);
+
 }  // namespace pdr

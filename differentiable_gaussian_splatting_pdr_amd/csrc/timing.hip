@@ -109,7 +109,8 @@ int pdr_splat_timing_read(double *total_ms, long long *launches, int reset) {
 const char *pdr_splat_kernel_name(int id) {
   static const char *names[PDR_KERNEL_COUNT] = {
       "preprocess", "bin_count", "scan", "bin_write",
-      "forward_raster", "zero_verify", "backward_raster", "finalize"};
+      "forward_raster", "zero_verify", "backward_raster", "finalize",
+      "loss_fwd", "loss_bwd", "loss_reduce"};
   return (id >= 0 && id < PDR_KERNEL_COUNT) ? names[id] : "unknown";
 }
 

@@ -164,3 +164,39 @@ class SplatRender(torch.autograd.Function):
 def render(params: torch.Tensor, H: int, W: int, radius: float = 3.0) -> torch.Tensor:
     """Differentiable render of [B, N, 5 + C] Gaussians to [B, H, W, C]."""
     return SplatRender.apply(params, H, W, radius)
+
+
+def l1_ssim_loss(image: torch.Tensor, target: torch.Tensor, lam: float = 0.2,
+                 c1: float = 1e-4, c2: float = 9e-4):
+    """(loss, dloss/dimage): the L1 + SSIM training loss of [B, H, W, C]
+    float32 frames, computed by the library's kernels (loss is a 0-d fp64
+    device tensor)."""
+    if image.shape != target.shape or image.dim() != 4:
+        raise ValueError("image and target must be [B, H, W, C] of the same shape")
+    if image.dtype != torch.float32 or target.dtype != torch.float32:
+        raise ValueError("image and target must be float32")
+    image, target = image.contiguous(), target.contiguous()
+    B, H, W, C = image.shape
+    dev = image.device
+    ws = torch.empty(_lib.pdr_loss_workspace_bytes(B, H, W, C), dtype=torch.uint8, device=dev)
+    grad = torch.empty_like(image)
+    loss = torch.empty((), dtype=torch.float64, device=dev)
+    _lib.pdr_loss_l1_ssim(image.data_ptr(), target.data_ptr(), B, H, W, C, lam, c1, c2,
+                          grad.data_ptr(), loss.data_ptr(), ws.data_ptr(), ws.numel(),
+                          _stream(dev))
+    return loss, grad
+
+
+class L1SSIMLoss(torch.autograd.Function):
+    """loss = (1 - lam) mean|I - T| + lam (1 - mean SSIM(I, T)); gradient to I."""
+
+    @staticmethod
+    def forward(ctx, image, target, lam=0.2):
+        loss, grad = l1_ssim_loss(image, target, lam)
+        ctx.save_for_backward(grad)
+        return loss.to(torch.float32)
+
+    @staticmethod
+    def backward(ctx, g):
+        (grad,) = ctx.saved_tensors
+        return grad * g.to(grad.dtype), None, None

@@ -138,3 +138,22 @@ def make_custom(B: int, N: int, H: int, W: int, C: int, seed: int,
     p[..., 5:] = amp_std * rng.standard_normal(size=(B, N, C))
     grad = rng.standard_normal(size=(B, H, W, C), dtype=np.float32)
     return p.astype(np.float32), grad
+
+
+def make_loss_inputs(B: int, H: int, W: int, C: int, seed: int, kind: str = "noisy"):
+    """Seeded (image, target) pairs in [0, 1]-like ranges for the training loss.
+
+    "noisy": target ~ U[0, 1], image = target + N(0, 0.1);
+    "flat":  target = 0.5 + N(0, 0.01), image = target + N(0, 0.005) (small
+             local variances, the hard case for single-precision moments).
+    """
+    rng = np.random.default_rng(seed)
+    if kind == "noisy":
+        t = rng.uniform(0.0, 1.0, size=(B, H, W, C))
+        x = t + 0.1 * rng.standard_normal(size=(B, H, W, C))
+    elif kind == "flat":
+        t = 0.5 + 0.01 * rng.standard_normal(size=(B, H, W, C))
+        x = t + 0.005 * rng.standard_normal(size=(B, H, W, C))
+    else:
+        raise ValueError(kind)
+    return x.astype(np.float32), t.astype(np.float32)

@@ -112,11 +112,36 @@ const char *pdr_splat_status_string(int status);
 enum pdr_kernel_id {
     PDR_K_PREPROCESS = 0, PDR_K_BIN_COUNT = 1, PDR_K_SCAN = 2, PDR_K_BIN_WRITE = 3,
     PDR_K_FORWARD_RASTER = 4, PDR_K_ZERO = 5, PDR_K_BACKWARD_RASTER = 6, PDR_K_FINALIZE = 7,
-    PDR_KERNEL_COUNT = 8
+    PDR_K_LOSS_FWD = 8, PDR_K_LOSS_BWD = 9, PDR_K_LOSS_REDUCE = 10,
+    PDR_KERNEL_COUNT = 11
 };
 int pdr_splat_timing(int enable);
 int pdr_splat_timing_read(double *total_ms, long long *launches, int reset);
 const char *pdr_splat_kernel_name(int id);
+
+/* ------------------------------------------------------------------------ */
+/* Training loss ("Learning Video Dynamics with Predictive Differentiable
+ * Rendering": the arXiv abstract says the model is optimised by a combined
+ * L1 and SSIM loss; the reading notes' "Method" section calls L1 + SSIM
+ * necessary).  Neither page gives the weighting or the SSIM window; this is
+ *
+ *   loss = (1 - lambda) * mean|I - T| + lambda * (1 - mean SSIM(I, T))
+ *
+ * with SSIM per frame and channel over the 11x11 Gaussian window of sigma
+ * 1.5 (weights summing to 1), zero padding outside the frame, stabilising
+ * constants c1, c2 (0.01^2 and 0.03^2 for data in [0, 1]), means over all
+ * B*H*W*C values, and d|u|/du = 0 at u = 0. */
+
+/* Workspace bytes of pdr_loss_l1_ssim (12 bytes per value plus 16 bytes
+ * per 32x32 tile, each part rounded up to 256); negative on invalid sizes. */
+long long pdr_loss_workspace_bytes(int B, int H, int W, int C);
+
+/* image, target [B][H][W][C] fp32 -> *loss (one fp64 value on the device)
+ * and grad_image [B][H][W][C] fp32 = dloss/dimage (overwritten).  Device
+ * pointers; 0 <= lambda <= 1; c1, c2 > 0.  Deterministic. */
+int pdr_loss_l1_ssim(const float *image, const float *target, int B, int H, int W, int C,
+                     float lambda, float c1, float c2, float *grad_image, double *loss,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -80,8 +80,10 @@ def ssim_map(x, y, c1=C1, c2=C2, win=WIN, sigma=SIGMA):
     return s, dict(mx=mx, my=my, a1=a1, a2=a2, b1=b1, b2=b2, g2=g2)
 
 
-def l1_ssim(image, target, lam=LAMBDA, c1=C1, c2=C2, win=WIN, sigma=SIGMA):
-    """Return (loss, dloss/dimage) in fp64 for [B,H,W,C] arrays."""
+def l1_ssim(image, target, lam=LAMBDA, c1=C1, c2=C2, win=WIN, sigma=SIGMA, with_mag=False):
+    """Return (loss, dloss/dimage) in fp64 for [B,H,W,C] arrays; with_mag adds
+    the per-value magnitude (sum of the absolute values of the gradient's
+    terms), the scale its rounding error refers to."""
     x = np.asarray(image, np.float64)
     y = np.asarray(target, np.float64)
     M = x.size
@@ -94,4 +96,9 @@ def l1_ssim(image, target, lam=LAMBDA, c1=C1, c2=C2, win=WIN, sigma=SIGMA):
     g2 = m["g2"]
     dssim = (_wsum(d_mu, g2) + 2 * x * _wsum(d_xx, g2) + y * _wsum(d_xy, g2)) / M
     grad = (1 - lam) * np.sign(x - y) / M - lam * dssim
-    return float(loss), grad
+    if not with_mag:
+        return float(loss), grad
+    mag = ((1 - lam) * np.abs(np.sign(x - y)) + lam * (
+        _wsum(np.abs(d_mu), g2) + 2 * np.abs(x) * _wsum(np.abs(d_xx), g2)
+        + np.abs(y) * _wsum(np.abs(d_xy), g2))) / M
+    return float(loss), grad, mag

@@ -19,7 +19,7 @@ FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced on the
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pdr_splat_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pdr_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_names():
@@ -29,7 +29,7 @@ def test_header_declares_the_binding_names():
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (pdr_splat_\w+)", out))
+    exported = set(re.findall(r"\bT (pdr_\w+)", out))
     missing = [f for f in declared_functions() if f not in exported]
     assert not missing, missing
     L = _lib.lib()
@@ -107,5 +107,29 @@ def test_timing_toggle_without_device():
     assert _lib.pdr_splat_timing(False) is True
     t = _lib.pdr_splat_timing_read(reset=True)
     assert set(t) == {"preprocess", "bin_count", "scan", "bin_write", "forward_raster",
-                      "zero_verify", "backward_raster", "finalize"}
+                      "zero_verify", "backward_raster", "finalize", "loss_fwd", "loss_bwd",
+                      "loss_reduce"}
     assert all(v == (0.0, 0) for v in t.values())
+
+
+def test_loss_entry_points_validate():
+    L = _lib.lib()
+    a = 256 * 1024
+    need = _lib.pdr_loss_workspace_bytes(2, 40, 33, 3)
+    M = 2 * 40 * 33 * 3
+    nblk = 2 * 2 * 2
+    assert need == -(-3 * M * 4 // 256) * 256 + -(-nblk * 16 // 256) * 256
+    with pytest.raises(_lib.PdrError):
+        _lib.pdr_loss_workspace_bytes(0, 4, 4, 1)
+    ok = dict(img=FAKE, tgt=FAKE, B=1, H=8, W=8, C=1, lam=0.2, c1=1e-4, c2=9e-4, grad=FAKE,
+              loss=FAKE, ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        d = dict(ok, **kw)
+        return L.pdr_loss_l1_ssim(d["img"], d["tgt"], d["B"], d["H"], d["W"], d["C"], d["lam"],
+                                  d["c1"], d["c2"], d["grad"], d["loss"], d["ws"], d["wsb"], None)
+    assert call(img=None) == -1 and call(loss=None) == -1 and call(ws=None) == -1
+    assert call(lam=-0.1) == -1 and call(lam=1.5) == -1 and call(lam=math.nan) == -1
+    assert call(c1=0.0) == -1 and call(c2=-1.0) == -1 and call(c2=math.inf) == -1
+    assert call(B=0) == -1 and call(C=0) == -1
+    assert call(ws=FAKE + 8) == -2 and call(wsb=16) == -2

@@ -1,0 +1,81 @@
+"""HIP L1 + SSIM loss vs the fp64 oracle (oracle/loss.py), on the GPU.
+
+Tolerance: loss value within 1e-5 relative; gradient elementwise within
+1e-4 of its magnitude (the sum of the absolute values of its terms, from
+the oracle) plus 1e-12 -- the loss gradient is a signed sum of window terms
+of size ~1/M, so its fp32 rounding error scales with that magnitude.
+"""
+import numpy as np
+import pytest
+
+from differentiable_gaussian_splatting_pdr_amd import workloads
+from oracle import loss as ol
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_loss(x, t, lam=0.2):
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import splat
+    xt = torch.from_numpy(x).cuda()
+    tt = torch.from_numpy(t).cuda()
+    loss, grad = splat.l1_ssim_loss(xt, tt, lam)
+    torch.cuda.synchronize()
+    return float(loss.cpu()), grad.cpu().numpy()
+
+
+def check(x, t, lam=0.2, frames=None, M_full=None):
+    lg, gg = gpu_loss(x, t, lam)
+    xs, ts = (x, t) if frames is None else (x[frames], t[frames])
+    lr, gr, mag = ol.l1_ssim(xs, ts, lam=lam, with_mag=True)
+    if frames is not None:
+        # the mean runs over all values: rescale the subset's gradient
+        scale = xs.size / M_full
+        gr, mag = gr * scale, mag * scale
+        gg = gg[frames]
+    else:
+        assert abs(lg - lr) <= 1e-5 * abs(lr) + 1e-7, (lg, lr)
+    err = np.abs(gg - gr)
+    bound = 1e-4 * mag + 1e-12
+    bad = err > bound
+    assert not bad.any(), (int(bad.sum()), float((err / bound).max()))
+    return float((err / bound).max())
+
+
+@pytest.mark.parametrize("shape,kind", [
+    ((1, 32, 32, 1), "noisy"), ((2, 37, 53, 3), "noisy"), ((1, 70, 45, 16), "noisy"),
+    ((3, 64, 64, 3), "flat"), ((1, 11, 7, 2), "noisy"), ((1, 1, 1, 1), "noisy"),
+])
+def test_loss_parity(shape, kind):
+    x, t = workloads.make_loss_inputs(*shape, seed=sum(shape), kind=kind)
+    print(shape, kind, check(x, t))
+
+
+@pytest.mark.parametrize("lam", [0.0, 1.0])
+def test_loss_weights(lam):
+    x, t = workloads.make_loss_inputs(2, 40, 40, 3, seed=5)
+    check(x, t, lam)
+
+
+def test_identical_frames():
+    x, _ = workloads.make_loss_inputs(2, 48, 48, 3, seed=6)
+    lg, gg = gpu_loss(x, x.copy())
+    assert abs(lg) < 1e-6 and np.abs(gg).max() < 1e-9
+
+
+def test_loss_benchmark_shape_sampled_frames():
+    # 384 frames of 128x128x3: the gradient on sampled frames
+    x, t = workloads.make_loss_inputs(384, 128, 128, 3, seed=7)
+    check(x, t, frames=[0, 191, 383], M_full=x.size)
+
+
+def test_loss_autograd():
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import splat
+    x, t = workloads.make_loss_inputs(2, 33, 31, 3, seed=8)
+    xt = torch.from_numpy(x).cuda().requires_grad_(True)
+    loss = splat.L1SSIMLoss.apply(xt, torch.from_numpy(t).cuda(), 0.2)
+    (2.0 * loss).backward()
+    _, gr, mag = ol.l1_ssim(x, t, with_mag=True)
+    err = np.abs(xt.grad.cpu().numpy() - 2 * gr)
+    assert np.all(err <= 2e-4 * mag + 1e-12)
