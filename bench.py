@@ -51,6 +51,16 @@ def kernel_bytes(B, N, H, W, C, pairs_tiles, T):
     }
 
 
+def loss_flops_bytes(B, H, W, C):
+    """Algorithmic work of the L1 + SSIM loss per launch pair, per value:
+    forward 3 products + 2 x (5 quantities x 11 taps x 2) window flops + 20
+    for SSIM and its three partials; gradient 2 x (3 x 11 x 2) + 8.  HBM:
+    forward reads I, T and writes three partial maps (20 B), gradient reads
+    the maps, I, T and writes dL/dI (24 B)."""
+    M = B * H * W * C
+    return {"loss_fwd": (M * (3 + 220 + 20), M * 20), "loss_bwd": (M * (132 + 8), M * 24)}
+
+
 def source_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -104,6 +114,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-loop", type=int, default=0,
                     help="only run this many steps (for rocprofv3), print nothing else")
+    ap.add_argument("--with-loss", action="store_true",
+                    help="with --profile-loop: also run the L1 + SSIM loss each step")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="with --profile-loop: also run one device-to-device copy of this many "
                          "MiB, the reference kernel for scaling HBM byte counters")
@@ -151,9 +163,25 @@ def main():
     if rc != 0:
         raise SystemExit("first step failed: %s" % _lib.status_string(rc))
 
+    # training loss on the rendered frames against a seeded synthetic target
+    _, target_np = workloads.make_loss_inputs(B, H, W, C, seed=1000 + args.workload)
+    target = torch.from_numpy(target_np).to(dev)
+    del target_np
+    loss_ws_bytes = _lib.pdr_loss_workspace_bytes(B, H, W, C)
+    loss_ws = torch.empty(loss_ws_bytes, dtype=torch.uint8, device=dev)
+    loss_val = torch.empty((), dtype=torch.float64, device=dev)
+    loss_grad = torch.empty_like(image)
+
+    def loss_step():
+        _lib.pdr_loss_l1_ssim(image.data_ptr(), target.data_ptr(), B, H, W, C, 0.2, 1e-4, 9e-4,
+                              loss_grad.data_ptr(), loss_val.data_ptr(), loss_ws.data_ptr(),
+                              loss_ws_bytes, st)
+
     if args.profile_loop:
         for _ in range(args.profile_loop):
             step()
+            if args.with_loss:
+                loss_step()
         if args.calib_copy_mb:
             n = args.calib_copy_mb << 20
             src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -194,6 +222,40 @@ def main():
     rc, _ = _lib.pdr_splat_check(ws.data_ptr(), st)
     if rc != 0:
         raise SystemExit("timed steps failed: %s" % _lib.status_string(rc))
+
+    # the loss: same K, HIP events around every launch
+    for _ in range(args.warmup):
+        loss_step()
+    _lib.pdr_splat_timing(True)
+    _lib.pdr_splat_timing_read(reset=True)
+    e0.record()
+    for _ in range(args.steps):
+        loss_step()
+    e1.record()
+    torch.cuda.synchronize()
+    loss_ms = e0.elapsed_time(e1) / args.steps
+    loss_kernels = _lib.pdr_splat_timing_read(reset=True)
+    _lib.pdr_splat_timing(False)
+    lfb = loss_flops_bytes(B, H, W, C)
+    loss_out = {"ms": round(loss_ms, 5), "values_per_s": B * H * W * C / (loss_ms * 1e-3),
+                "lambda": 0.2, "kernels": {}}
+    for name in ("loss_fwd", "loss_bwd", "loss_reduce"):
+        tot, cnt = loss_kernels[name]
+        if not cnt:
+            continue
+        avg = tot / cnt
+        row = {"avg_ms": round(avg, 5)}
+        if name in lfb:
+            fl, by = lfb[name]
+            row["alg_TFLOPs"] = round(fl / (avg * 1e-3) / 1e12, 3)
+            row["alg_GBps"] = round(by / (avg * 1e-3) / 1e9, 1)
+        loss_out["kernels"][name] = row
+    ldom = max(lfb, key=lambda k: loss_out["kernels"][k]["avg_ms"])
+    lach = loss_out["kernels"][ldom]["alg_TFLOPs"]
+    loss_out["roofline"] = {"bound": "alu", "kernel": ldom, "achieved": lach,
+                            "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(lach / FP32_PEAK_TFLOPS, 4),
+                            "hbm_frac": round(loss_out["kernels"][ldom]["alg_GBps"] / HBM_PEAK_GBS, 4)}
 
     cpu, support_pairs = None, None
     if not args.no_cpu_baseline:
@@ -256,6 +318,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "loss": loss_out,
     }
     print(json.dumps(out), flush=True)
 

@@ -138,6 +138,7 @@ int pdr_splat_check(void *workspace, void *stream, long long *pairs_needed) {
 long long pdr_loss_workspace_bytes(int B, int H, int W, int C) {
   if (B < 1 || H < 1 || W < 1 || C < 1) return PDR_ERR_INVALID_ARG;
   if ((long long)B * H * W * C > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
+  if ((long long)H * W * C >= (1LL << 29)) return PDR_ERR_INVALID_ARG;  // 32-bit frame offsets
   return (long long)loss_workspace_bytes(B, H, W, C);
 }
 

@@ -132,13 +132,15 @@ const char *pdr_splat_kernel_name(int id);
  * constants c1, c2 (0.01^2 and 0.03^2 for data in [0, 1]), means over all
  * B*H*W*C values, and d|u|/du = 0 at u = 0. */
 
-/* Workspace bytes of pdr_loss_l1_ssim (12 bytes per value plus 16 bytes
- * per 32x32 tile, each part rounded up to 256); negative on invalid sizes. */
+/* Workspace bytes of pdr_loss_l1_ssim (12 bytes per value for three
+ * per-pixel partial-derivative maps, plus 16 bytes per workgroup of the
+ * forward pass, each part rounded up to 256); negative on invalid sizes. */
 long long pdr_loss_workspace_bytes(int B, int H, int W, int C);
 
 /* image, target [B][H][W][C] fp32 -> *loss (one fp64 value on the device)
  * and grad_image [B][H][W][C] fp32 = dloss/dimage (overwritten).  Device
- * pointers; 0 <= lambda <= 1; c1, c2 > 0.  Deterministic. */
+ * pointers; 0 <= lambda <= 1; c1, c2 > 0; B*H*W*C < 2^31 and one frame
+ * H*W*C < 2^29 values (PDR_ERR_INVALID_ARG otherwise).  Deterministic. */
 int pdr_loss_l1_ssim(const float *image, const float *target, int B, int H, int W, int C,
                      float lambda, float c1, float c2, float *grad_image, double *loss,
                      void *workspace, size_t workspace_bytes, void *stream);

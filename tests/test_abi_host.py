@@ -117,10 +117,14 @@ def test_loss_entry_points_validate():
     a = 256 * 1024
     need = _lib.pdr_loss_workspace_bytes(2, 40, 33, 3)
     M = 2 * 40 * 33 * 3
-    nblk = 2 * 2 * 2
-    assert need == -(-3 * M * 4 // 256) * 256 + -(-nblk * 16 // 256) * 256
+    # three partial maps, then one (s, |x - y|) fp64 pair per workgroup
+    assert need % 256 == 0 and need >= -(-3 * M * 4 // 256) * 256 + 256
+    assert need <= -(-3 * M * 4 // 256) * 256 + -(-M * 16 // 256) * 256
     with pytest.raises(_lib.PdrError):
         _lib.pdr_loss_workspace_bytes(0, 4, 4, 1)
+    with pytest.raises(_lib.PdrError):   # one frame of 2^29 values
+        _lib.pdr_loss_workspace_bytes(1, 1 << 15, 1 << 14, 1)
+    assert _lib.pdr_loss_workspace_bytes(1, 1 << 15, (1 << 14) - 1, 1) > 0
     ok = dict(img=FAKE, tgt=FAKE, B=1, H=8, W=8, C=1, lam=0.2, c1=1e-4, c2=9e-4, grad=FAKE,
               loss=FAKE, ws=FAKE, wsb=1 << 20)
 
