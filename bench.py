@@ -92,6 +92,11 @@ def cpu_baseline_leg(params, grad, wl, radius, budget_s, want_count=True):
     _, _, _, pairs = oracle.render(sp, wl.H, wl.W, radius, extras=False, nthreads=threads)
     oracle.grad(sp, sg, wl.H, wl.W, radius, extras=False, nthreads=threads)
     dt = time.perf_counter() - t0
+    # one frame on one thread
+    t1 = time.perf_counter()
+    _, _, _, p1 = oracle.render(params[:1], wl.H, wl.W, radius, extras=False, nthreads=1)
+    oracle.grad(params[:1], grad[:1], wl.H, wl.W, radius, extras=False, nthreads=1)
+    dt1 = time.perf_counter() - t1
     return {
         "value": float(pairs.sum()) / dt,
         "unit": "evals/s",
@@ -99,6 +104,7 @@ def cpu_baseline_leg(params, grad, wl, radius, budget_s, want_count=True):
         "kind": "oracle",
         "sample": "%d of %d frames, forward+backward, fp64 C, %.2f s wall" % (frames, wl.B, dt),
         "frames_per_s": frames / dt,
+        "one_thread_evals_per_s": float(p1.sum()) / dt1,
     }, total_pairs
 
 
@@ -113,7 +119,8 @@ def main():
                     help="target wall seconds of the oracle baseline run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-loop", type=int, default=0,
-                    help="only run this many steps (for rocprofv3), print nothing else")
+                    help="only run --warmup and then this many steps (for rocprofv3), print "
+                         "nothing else")
     ap.add_argument("--with-loss", action="store_true",
                     help="with --profile-loop: also run the L1 + SSIM loss each step")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -178,7 +185,9 @@ def main():
                               loss_ws_bytes, st)
 
     if args.profile_loop:
-        for _ in range(args.profile_loop):
+        # warm-up steps first (the clocks ramp over the first launches), then
+        # the profiled steps; summaries use the last profile_loop dispatches
+        for _ in range(args.warmup + args.profile_loop):
             step()
             if args.with_loss:
                 loss_step()

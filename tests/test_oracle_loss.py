@@ -88,3 +88,22 @@ def test_gradient_central_differences(lam):
         xm[idx] -= h
         fd = (ol.l1_ssim(xp, y, lam=lam)[0] - ol.l1_ssim(xm, y, lam=lam)[0]) / (2 * h)
         assert abs(fd - grad[idx]) <= 1e-6 * abs(grad[idx]) + 1e-10, (idx, fd, grad[idx])
+
+
+def test_ssim_symmetric_and_bounded():
+    rng = np.random.default_rng(5)
+    x = rng.uniform(0, 1, (1, 14, 12, 2))
+    y = rng.uniform(0, 1, (1, 14, 12, 2))
+    s1, _ = ol.ssim_map(x, y)
+    s2, _ = ol.ssim_map(y, x)
+    assert np.abs(s1 - s2).max() < 1e-15
+    assert np.all(s1 <= 1.0) and np.all(s1 >= -1.0)
+
+
+def test_gradient_magnitude_bounds_gradient():
+    rng = np.random.default_rng(6)
+    x = rng.uniform(0, 1, (1, 12, 13, 3))
+    y = np.clip(x + 0.1 * rng.standard_normal(x.shape), 0, 1)
+    _, g, mag = ol.l1_ssim(x, y, with_mag=True)
+    assert np.all(np.abs(g) <= mag * (1 + 1e-12))
+    assert np.all(mag > 0)
