@@ -33,9 +33,14 @@ EXPORTED = (
     "pdr_splat_kernel_name",
     "pdr_loss_workspace_bytes",
     "pdr_loss_l1_ssim",
+    "pdr_splat_forward_concat",
+    "pdr_splat_backward_concat",
+    "pdr_grid_init",
+    "pdr_params_activate",
+    "pdr_params_activate_backward",
 )
 
-KERNEL_COUNT = 11
+KERNEL_COUNT = 14
 
 
 class PdrError(RuntimeError):
@@ -80,6 +85,17 @@ def lib() -> ctypes.CDLL:
         L.pdr_loss_workspace_bytes.restype = ll
         L.pdr_loss_l1_ssim.argtypes = [vp, vp, i, i, i, i, f, f, f, vp, vp, vp, sz, vp]
         L.pdr_loss_l1_ssim.restype = i
+        L.pdr_splat_forward_concat.argtypes = [vp, vp, i, vp, i, i, i, i, i, f, vp, sz, vp]
+        L.pdr_splat_forward_concat.restype = i
+        L.pdr_splat_backward_concat.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, f, vp, sz, i,
+                                                vp]
+        L.pdr_splat_backward_concat.restype = i
+        L.pdr_grid_init.argtypes = [vp, i, i, i, i, i, i, f, vp, vp]
+        L.pdr_grid_init.restype = i
+        L.pdr_params_activate.argtypes = [vp, vp, i, i, i, i, i, i, vp]
+        L.pdr_params_activate.restype = i
+        L.pdr_params_activate_backward.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+        L.pdr_params_activate_backward.restype = i
         _lib = L
     return _lib
 
@@ -154,3 +170,34 @@ def pdr_loss_l1_ssim(image, target, B, H, W, C, lam, c1, c2, grad_image, loss, w
     return _raise(lib().pdr_loss_l1_ssim(image, target, B, H, W, C, float(lam), float(c1),
                                          float(c2), grad_image, loss, workspace, workspace_bytes,
                                          stream), "pdr_loss_l1_ssim")
+
+
+def pdr_splat_forward_concat(params, pixel, Cp, out, B, N, H, W, C, radius, workspace,
+                             workspace_bytes, stream):
+    return _raise(lib().pdr_splat_forward_concat(params, pixel, Cp, out, B, N, H, W, C,
+                                                 float(radius), workspace, workspace_bytes,
+                                                 stream), "pdr_splat_forward_concat")
+
+
+def pdr_splat_backward_concat(params, grad_out, Cp, grad_params, grad_pixel, B, N, H, W, C,
+                              radius, workspace, workspace_bytes, reuse_binning, stream):
+    return _raise(lib().pdr_splat_backward_concat(params, grad_out, Cp, grad_params, grad_pixel,
+                                                  B, N, H, W, C, float(radius), workspace,
+                                                  workspace_bytes, int(reuse_binning), stream),
+                  "pdr_splat_backward_concat")
+
+
+def pdr_grid_init(raw, B, gx, gy, H, W, C, init_scale, image, stream):
+    return _raise(lib().pdr_grid_init(raw, B, gx, gy, H, W, C, float(init_scale), image, stream),
+                  "pdr_grid_init")
+
+
+def pdr_params_activate(raw, params, B, gx, gy, H, W, C, stream):
+    return _raise(lib().pdr_params_activate(raw, params, B, gx, gy, H, W, C, stream),
+                  "pdr_params_activate")
+
+
+def pdr_params_activate_backward(raw, grad_params, grad_raw, B, gx, gy, H, W, C, stream):
+    return _raise(lib().pdr_params_activate_backward(raw, grad_params, grad_raw, B, gx, gy, H, W,
+                                                     C, stream),
+                  "pdr_params_activate_backward")

@@ -53,6 +53,61 @@ int layout_for(const Dims &d, void *ws, size_t bytes, Layout *L) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PDR_OK : PDR_ERR_HIP; }
 
+// Forward (binning + raster) into image with Cp leading pixel-branch
+// channels per pixel (Cp = 0: the plain layout).
+int forward_impl(const float *params, const float *pixel, int Cp, float *image, int B, int N,
+                 int H, int W, int C, float radius, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+  Dims d;
+  Layout L;
+  if (!params || !image) return PDR_ERR_INVALID_ARG;
+  int rc = validate_sizes(B, N, H, W, C, &d);
+  if (rc == PDR_OK) rc = validate_radius(radius);
+  if (rc == PDR_OK && (long long)B * H * W * (Cp + (long long)C) > (1LL << 46)) rc = PDR_ERR_INVALID_ARG;
+  if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
+  if (rc != PDR_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char *w = (char *)workspace;
+  hipError_t e = launch_binning(params, B, N, H, W, C, radius, workspace, L, (int *)(w + L.tile_off),
+                                (int *)(w + L.list), L.cap, true, st);
+  if (e == hipSuccess)
+    e = launch_forward_raster(params, image, B, N, H, W, C, radius, workspace, L, st, pixel, Cp);
+  return hip_status(e);
+}
+
+int backward_impl(const float *params, const float *grad_image, int Cp, float *grad_params,
+                  float *grad_pixel, int B, int N, int H, int W, int C, float radius,
+                  void *workspace, size_t workspace_bytes, int reuse_binning, void *stream) {
+  Dims d;
+  Layout L;
+  if (!params || !grad_image || !grad_params) return PDR_ERR_INVALID_ARG;
+  int rc = validate_sizes(B, N, H, W, C, &d);
+  if (rc == PDR_OK) rc = validate_radius(radius);
+  if (rc == PDR_OK && (long long)B * H * W * (Cp + (long long)C) > (1LL << 46)) rc = PDR_ERR_INVALID_ARG;
+  if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
+  if (rc != PDR_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char *w = (char *)workspace;
+  hipError_t e = hipSuccess;
+  if (!reuse_binning)
+    e = launch_binning(params, B, N, H, W, C, radius, workspace, L, (int *)(w + L.tile_off),
+                       (int *)(w + L.list), L.cap, true, st);
+  if (e == hipSuccess)
+    e = launch_backward(params, grad_image, grad_params, B, N, H, W, C, radius, workspace, L,
+                        reuse_binning != 0, st, grad_pixel, Cp);
+  return hip_status(e);
+}
+
+// Grid of gx x gy Gaussians per frame over an H x W x C frame.
+int validate_grid(int B, int gx, int gy, int H, int W, int C) {
+  if (B < 1 || gx < 1 || gy < 1 || H < 1 || W < 1 || C < 1) return PDR_ERR_INVALID_ARG;
+  if (H > kMaxHW || W > kMaxHW) return PDR_ERR_INVALID_ARG;
+  const long long N = (long long)gx * gy;
+  if (N > kMaxN) return PDR_ERR_INVALID_ARG;
+  if ((long long)B * N * (5 + (long long)C) > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
+  return PDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,41 +124,59 @@ long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long
 
 int pdr_splat_forward(const float *params, float *image, int B, int N, int H, int W, int C,
                       float radius, void *workspace, size_t workspace_bytes, void *stream) {
-  Dims d;
-  Layout L;
-  if (!params || !image) return PDR_ERR_INVALID_ARG;
-  int rc = validate_sizes(B, N, H, W, C, &d);
-  if (rc == PDR_OK) rc = validate_radius(radius);
-  if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
-  if (rc != PDR_OK) return rc;
-  hipStream_t st = (hipStream_t)stream;
-  char *w = (char *)workspace;
-  hipError_t e = launch_binning(params, B, N, H, W, C, radius, workspace, L, (int *)(w + L.tile_off),
-                                (int *)(w + L.list), L.cap, true, st);
-  if (e == hipSuccess) e = launch_forward_raster(params, image, B, N, H, W, C, radius, workspace, L, st);
-  return hip_status(e);
+  return forward_impl(params, nullptr, 0, image, B, N, H, W, C, radius, workspace, workspace_bytes,
+                      stream);
 }
 
 int pdr_splat_backward(const float *params, const float *grad_image, float *grad_params, int B,
                        int N, int H, int W, int C, float radius, void *workspace,
                        size_t workspace_bytes, int reuse_binning, void *stream) {
-  Dims d;
-  Layout L;
-  if (!params || !grad_image || !grad_params) return PDR_ERR_INVALID_ARG;
-  int rc = validate_sizes(B, N, H, W, C, &d);
-  if (rc == PDR_OK) rc = validate_radius(radius);
-  if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
+  return backward_impl(params, grad_image, 0, grad_params, nullptr, B, N, H, W, C, radius,
+                       workspace, workspace_bytes, reuse_binning, stream);
+}
+
+int pdr_splat_forward_concat(const float *params, const float *pixel, int Cp, float *out, int B,
+                             int N, int H, int W, int C, float radius, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  if (Cp < 0 || (Cp > 0 && !pixel)) return PDR_ERR_INVALID_ARG;
+  return forward_impl(params, pixel, Cp, out, B, N, H, W, C, radius, workspace, workspace_bytes,
+                      stream);
+}
+
+int pdr_splat_backward_concat(const float *params, const float *grad_out, int Cp,
+                              float *grad_params, float *grad_pixel, int B, int N, int H, int W,
+                              int C, float radius, void *workspace, size_t workspace_bytes,
+                              int reuse_binning, void *stream) {
+  if (Cp < 0) return PDR_ERR_INVALID_ARG;
+  return backward_impl(params, grad_out, Cp, grad_params, grad_pixel, B, N, H, W, C, radius,
+                       workspace, workspace_bytes, reuse_binning, stream);
+}
+
+int pdr_grid_init(float *raw, int B, int gx, int gy, int H, int W, int C, float init_scale,
+                  const float *image, void *stream) {
+  if (!raw) return PDR_ERR_INVALID_ARG;
+  int rc = validate_grid(B, gx, gy, H, W, C);
   if (rc != PDR_OK) return rc;
-  hipStream_t st = (hipStream_t)stream;
-  char *w = (char *)workspace;
-  hipError_t e = hipSuccess;
-  if (!reuse_binning)
-    e = launch_binning(params, B, N, H, W, C, radius, workspace, L, (int *)(w + L.tile_off),
-                       (int *)(w + L.list), L.cap, true, st);
-  if (e == hipSuccess)
-    e = launch_backward(params, grad_image, grad_params, B, N, H, W, C, radius, workspace, L,
-                        reuse_binning != 0, st);
-  return hip_status(e);
+  if (!(init_scale > 0.f) || !isfinite(init_scale)) return PDR_ERR_INVALID_ARG;
+  return hip_status(launch_grid_init(raw, B, gx, gy, H, W, C, init_scale, image,
+                                     (hipStream_t)stream));
+}
+
+int pdr_params_activate(const float *raw, float *params, int B, int gx, int gy, int H, int W,
+                        int C, void *stream) {
+  if (!raw || !params) return PDR_ERR_INVALID_ARG;
+  int rc = validate_grid(B, gx, gy, H, W, C);
+  if (rc != PDR_OK) return rc;
+  return hip_status(launch_activate(raw, params, B, gx, gy, H, W, C, (hipStream_t)stream));
+}
+
+int pdr_params_activate_backward(const float *raw, const float *grad_params, float *grad_raw,
+                                 int B, int gx, int gy, int H, int W, int C, void *stream) {
+  if (!raw || !grad_params || !grad_raw) return PDR_ERR_INVALID_ARG;
+  int rc = validate_grid(B, gx, gy, H, W, C);
+  if (rc != PDR_OK) return rc;
+  return hip_status(launch_activate_backward(raw, grad_params, grad_raw, B, gx, gy, H, W, C,
+                                             (hipStream_t)stream));
 }
 
 int pdr_splat_bin(const float *params, int B, int N, int H, int W, int C, float radius,

@@ -29,20 +29,34 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
                           void *ws, const Layout &L, int *tile_off, int *list, long long cap,
                           bool stamp_valid, hipStream_t st);
 
-// Forward raster: image[b][y][x][c] for all channels.
+// Forward raster: image[b][y][x][c] for all channels.  With Cp > 0 the
+// output has Cp + C channels per pixel: pixel[b][y][x][0..Cp) first, then the
+// rendered channels (concat fusion).
 hipError_t launch_forward_raster(const float *params, float *image, int B, int N, int H, int W,
-                                 int C, float radius, void *ws, const Layout &L, hipStream_t st);
+                                 int C, float radius, void *ws, const Layout &L, hipStream_t st,
+                                 const float *pixel = nullptr, int Cp = 0);
 
 // Backward: zero grad_params (and verify the binning stamp when reusing),
 // raster the per-Gaussian sums with one atomic per wave per Gaussian, then
 // turn the sums into gradients in place.
+// With Cp > 0, grad_image has Cp + C channels per pixel; the first Cp are
+// copied to grad_pixel (if not null), the rest drive the renderer.
 hipError_t launch_backward(const float *params, const float *grad_image, float *grad_params, int B,
                            int N, int H, int W, int C, float radius, void *ws, const Layout &L,
-                           bool check_stamp, hipStream_t st);
+                           bool check_stamp, hipStream_t st, float *grad_pixel = nullptr,
+                           int Cp = 0);
 
 // L1 + SSIM loss: grad = dloss/dimage, *loss on the device.
 hipError_t launch_loss(const float *img, const float *tgt, int B, int H, int W, int C, float lam,
                        float c1, float c2, float *grad, double *loss, void *ws, hipStream_t st);
 size_t loss_workspace_bytes(int B, int H, int W, int C);
+
+// Adapter-side ops: grid initialisation, activation and its gradient.
+hipError_t launch_grid_init(float *raw, int B, int gx, int gy, int H, int W, int C, float s0,
+                            const float *image, hipStream_t st);
+hipError_t launch_activate(const float *raw, float *params, int B, int gx, int gy, int H, int W,
+                           int C, hipStream_t st);
+hipError_t launch_activate_backward(const float *raw, const float *grad_params, float *grad_raw,
+                                    int B, int gx, int gy, int H, int W, int C, hipStream_t st);
 
 }  // namespace pdr

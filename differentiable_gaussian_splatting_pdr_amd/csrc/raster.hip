@@ -98,11 +98,22 @@ __device__ __forceinline__ void stage_entry(Entry<CP> *s, const GRec *__restrict
   }
 }
 
+// Where the image (forward output, backward input) lives: value (pixel, c)
+// at pixel * ldo + ooff + c.  With concat fusion (ldo = Cp + C, ooff = Cp)
+// the first Cp channels of every pixel belong to the pixel branch: the
+// forward copies them from xin, the backward copies their gradient to xout.
+struct ImgView {
+  int ldo, ooff;
+  const float *xin;
+  float *xout;
+  int Cp;
+};
+
 template <int CP, int UW, int UX, int UY>
 __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
     const GRec *__restrict__ recs, const float *__restrict__ params,
     const int *__restrict__ tile_off, const int *__restrict__ list, int B, int N, int H, int W,
-    int C, int c0, int cc, float thr, int nTx, int nT, float *__restrict__ image,
+    int C, int c0, int cc, float thr, int nTx, int nT, float *__restrict__ image, ImgView iv,
     const WsHeader *hdr) {
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
@@ -167,10 +178,16 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
     for (int i = 0; i < UX; ++i) {
       const int px = rx0 + UW * i + lx, py = ry0 + UH * j + ly;
       if (px < W && py < H) {
-        float *o = image + (((size_t)f * H + py) * W + px) * (size_t)C + c0;
+        const size_t pix = ((size_t)f * H + py) * W + px;
+        float *o = image + pix * (size_t)iv.ldo + iv.ooff + c0;
 #pragma unroll
         for (int c = 0; c < CP; ++c)
           if (c < cc) o[c] = acc[j][i][c];
+        if (iv.xin) {   // concat fusion: the pixel branch's channels go first
+          const float *xi = iv.xin + pix * (size_t)iv.Cp;
+          float *ob = image + pix * (size_t)iv.ldo;
+          for (int c = 0; c < iv.Cp; ++c) ob[c] = xi[c];
+        }
       }
     }
   }
@@ -224,7 +241,7 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
     const GRec *__restrict__ recs, const float *__restrict__ params,
     const float *__restrict__ gimg, const int *__restrict__ tile_off,
     const int *__restrict__ list, int B, int N, int H, int W, int C, int c0, int cc, float thr,
-    int nTx, int nT, float *__restrict__ sums, const WsHeader *hdr) {
+    int nTx, int nT, float *__restrict__ sums, ImgView iv, const WsHeader *hdr) {
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
   constexpr int K = CP + 5;
@@ -251,10 +268,15 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
     for (int i = 0; i < UX; ++i) {
       const int px = rx0 + UW * i + lx, py = ry0 + UH * j + ly;
       const bool in = px < W && py < H;
-      const float *g =
-          gimg + (((size_t)f * H + (in ? py : 0)) * W + (in ? px : 0)) * (size_t)C + c0;
+      const size_t pix = ((size_t)f * H + (in ? py : 0)) * W + (in ? px : 0);
+      const float *g = gimg + pix * (size_t)iv.ldo + iv.ooff + c0;
 #pragma unroll
       for (int c = 0; c < CP; ++c) G[j][i][c] = (in && c < cc) ? g[c] : 0.f;
+      if (iv.xout && in) {   // concat fusion: the pixel branch's gradient slice
+        const float *gb = gimg + pix * (size_t)iv.ldo;
+        float *xo = iv.xout + pix * (size_t)iv.Cp;
+        for (int c = 0; c < iv.Cp; ++c) xo[c] = gb[c];
+      }
     }
   }
   const int vidx = value_index<KP>(lane & (KP - 1));
@@ -390,6 +412,7 @@ struct RasterArgs {
   float thr;
   int nTx, nT;
   float *out;
+  ImgView iv;
   const WsHeader *hdr;
 };
 
@@ -400,7 +423,7 @@ void fwd_cp(const RasterArgs &a, hipStream_t st) {
   PDR_TIMED(PDR_K_FORWARD_RASTER, st,
             hipLaunchKernelGGL((k_forward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
                                a.recs, a.params, a.tile_off, a.list, a.B, a.N, a.H, a.W, a.C,
-                               a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.hdr));
+                               a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr));
 }
 
 template <int CP, int UW, int UX, int UY>
@@ -410,7 +433,7 @@ void bwd_cp(const RasterArgs &a, hipStream_t st) {
   PDR_TIMED(PDR_K_BACKWARD_RASTER, st,
             hipLaunchKernelGGL((k_backward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
                                a.recs, a.params, a.gimg, a.tile_off, a.list, a.B, a.N, a.H, a.W,
-                               a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.hdr));
+                               a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr));
 }
 
 // Unit shape and units per wave (compile-time tuning knob): 8x8 quads,
@@ -460,6 +483,7 @@ RasterArgs raster_args(const float *params, int B, int N, int H, int W, int C, f
   a.nTx = (W + kTileW - 1) / kTileW;
   a.nT = a.nTx * ((H + kTileH - 1) / kTileH);
   a.out = nullptr;
+  a.iv = ImgView{C, 0, nullptr, nullptr, 0};
   a.hdr = (const WsHeader *)(w + L.hdr);
   return a;
 }
@@ -467,12 +491,15 @@ RasterArgs raster_args(const float *params, int B, int N, int H, int W, int C, f
 }  // namespace
 
 hipError_t launch_forward_raster(const float *params, float *image, int B, int N, int H, int W,
-                                 int C, float radius, void *ws, const Layout &L, hipStream_t st) {
+                                 int C, float radius, void *ws, const Layout &L, hipStream_t st,
+                                 const float *pixel, int Cp) {
   RasterArgs a = raster_args(params, B, N, H, W, C, radius, ws, L);
   a.out = image;
+  a.iv = ImgView{Cp + C, Cp, nullptr, nullptr, Cp};
   for (int c0 = 0; c0 < C; c0 += 16) {
     a.c0 = c0;
     a.cc = C - c0 < 16 ? C - c0 : 16;
+    a.iv.xin = (c0 == 0 && Cp > 0) ? pixel : nullptr;   // copied once
     dispatch<false>(a, st);
   }
   return hipGetLastError();
@@ -480,8 +507,9 @@ hipError_t launch_forward_raster(const float *params, float *image, int B, int N
 
 hipError_t launch_backward(const float *params, const float *grad_image, float *grad_params, int B,
                            int N, int H, int W, int C, float radius, void *ws, const Layout &L,
-                           bool check_stamp, hipStream_t st) {
+                           bool check_stamp, hipStream_t st, float *grad_pixel, int Cp) {
   RasterArgs a = raster_args(params, B, N, H, W, C, radius, ws, L);
+  a.iv = ImgView{Cp + C, Cp, nullptr, nullptr, Cp};
   WsHeader *hdr = (WsHeader *)((char *)ws + L.hdr);
   long long BN = (long long)B * N, total = BN * (5 + C);
   long long zb = (total + 255) / 256;
@@ -495,6 +523,7 @@ hipError_t launch_backward(const float *params, const float *grad_image, float *
   for (int c0 = 0; c0 < C; c0 += 16) {
     a.c0 = c0;
     a.cc = C - c0 < 16 ? C - c0 : 16;
+    a.iv.xout = (c0 == 0 && Cp > 0) ? grad_pixel : nullptr;   // copied once
     dispatch<true>(a, st);
   }
   PDR_TIMED(PDR_K_FINALIZE, st,

@@ -110,7 +110,7 @@ const char *pdr_splat_kernel_name(int id) {
   static const char *names[PDR_KERNEL_COUNT] = {
       "preprocess", "bin_count", "scan", "bin_write",
       "forward_raster", "zero_verify", "backward_raster", "finalize",
-      "loss_fwd", "loss_bwd", "loss_reduce"};
+      "loss_fwd", "loss_bwd", "loss_reduce", "grid_init", "activate", "activate_bwd"};
   return (id >= 0 && id < PDR_KERNEL_COUNT) ? names[id] : "unknown";
 }
 

@@ -200,3 +200,137 @@ class L1SSIMLoss(torch.autograd.Function):
     def backward(ctx, g):
         (grad,) = ctx.saved_tensors
         return grad * g.to(grad.dtype), None, None
+
+
+# --------------------------------------------------------------- concat fusion
+
+def forward_concat(params: torch.Tensor, pixel: torch.Tensor, H: int, W: int, radius: float = 3.0,
+                   workspace: Workspace | None = None):
+    """[pixel | render(params)] along channels: out [B, H, W, Cp + C], written
+    by the forward raster (no separate concat).  Returns (out, workspace)."""
+    B, N, C = _check_params(params)
+    if pixel.dim() != 4 or pixel.shape[:3] != (B, H, W) or pixel.dtype != torch.float32:
+        raise ValueError("pixel must be float32 [B, H, W, Cp]")
+    pixel = pixel.contiguous()
+    Cp = pixel.shape[3]
+    dev = params.device
+    ws = workspace or Workspace(dev)
+    ws.ensure(Workspace.bytes_for(B, N, H, W, C, _initial_pairs(B, N, H, W)))
+    out = torch.empty((B, H, W, Cp + C), dtype=torch.float32, device=dev)
+    st = _stream(dev)
+    for _ in range(2):
+        _lib.pdr_splat_forward_concat(params.data_ptr(), pixel.data_ptr(), Cp, out.data_ptr(), B, N,
+                                      H, W, C, radius, ws.ptr, ws.nbytes, st)
+        rc, need = _lib.pdr_splat_check(ws.ptr, st)
+        if rc == _lib.PDR_OK:
+            return out, ws
+        if rc != _lib.PDR_ERR_OVERFLOW:
+            raise _lib.PdrError(rc, "pdr_splat_forward_concat")
+        ws.ensure(Workspace.bytes_for(B, N, H, W, C, need))
+    raise _lib.PdrError(_lib.PDR_ERR_OVERFLOW, "pdr_splat_forward_concat")
+
+
+def backward_concat(params: torch.Tensor, grad_out: torch.Tensor, Cp: int, H: int, W: int,
+                    radius: float = 3.0, workspace: Workspace | None = None,
+                    reuse_binning: bool = False, want_pixel_grad: bool = True):
+    """(dL/dparams, dL/dpixel or None) from dL/dout [B, H, W, Cp + C]."""
+    B, N, C = _check_params(params)
+    if grad_out.shape != (B, H, W, Cp + C) or grad_out.dtype != torch.float32:
+        raise ValueError("grad_out must be float32 [B, H, W, Cp + C]")
+    grad_out = grad_out.contiguous()
+    dev = params.device
+    grad_params = torch.empty_like(params)
+    grad_pixel = (torch.empty((B, H, W, Cp), dtype=torch.float32, device=dev)
+                  if want_pixel_grad and Cp > 0 else None)
+    st = _stream(dev)
+    if workspace is None:
+        reuse_binning = False
+        workspace = Workspace(dev, Workspace.bytes_for(B, N, H, W, C, _initial_pairs(B, N, H, W)))
+    for _ in range(2):
+        _lib.pdr_splat_backward_concat(params.data_ptr(), grad_out.data_ptr(), Cp,
+                                       grad_params.data_ptr(),
+                                       grad_pixel.data_ptr() if grad_pixel is not None else None,
+                                       B, N, H, W, C, radius, workspace.ptr, workspace.nbytes,
+                                       int(reuse_binning), st)
+        rc, need = _lib.pdr_splat_check(workspace.ptr, st)
+        if rc == _lib.PDR_OK:
+            return grad_params, grad_pixel
+        if rc not in (_lib.PDR_ERR_OVERFLOW, _lib.PDR_ERR_STALE):
+            raise _lib.PdrError(rc, "pdr_splat_backward_concat")
+        if rc == _lib.PDR_ERR_OVERFLOW:
+            workspace.ensure(Workspace.bytes_for(B, N, H, W, C, need))
+        reuse_binning = False
+    raise _lib.PdrError(rc, "pdr_splat_backward_concat")
+
+
+class SplatRenderConcat(torch.autograd.Function):
+    """out = [pixel | render(params)]; backward reuses the forward's binning."""
+
+    @staticmethod
+    def forward(ctx, params, pixel, H, W, radius):
+        params = params.contiguous()
+        out, ws = forward_concat(params, pixel, H, W, radius)
+        ctx.save_for_backward(params)
+        ctx.meta = (H, W, radius, ws, pixel.shape[3])
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        (params,) = ctx.saved_tensors
+        H, W, radius, ws, Cp = ctx.meta
+        gp, gx = backward_concat(params, grad_out.contiguous(), Cp, H, W, radius, workspace=ws,
+                                 reuse_binning=True, want_pixel_grad=ctx.needs_input_grad[1])
+        return gp, gx, None, None, None
+
+
+def render_concat(params, pixel, H: int, W: int, radius: float = 3.0):
+    return SplatRenderConcat.apply(params, pixel, H, W, radius)
+
+
+# ------------------------------------------------------ grid and activations
+
+def grid_init(B: int, gx: int, gy: int, H: int, W: int, C: int, init_scale: float = 0.5,
+              image: torch.Tensor | None = None, device="cuda"):
+    """Raw parameters [B, gx*gy, 5 + C] that activate onto the grid centres
+    (scales init_scale * cell, theta 0, amplitudes from image or 0)."""
+    dev = torch.device(device) if image is None else image.device
+    raw = torch.empty((B, gx * gy, 5 + C), dtype=torch.float32, device=dev)
+    if image is not None:
+        if image.shape != (B, H, W, C) or image.dtype != torch.float32:
+            raise ValueError("image must be float32 [B, H, W, C]")
+        image = image.contiguous()
+    _lib.pdr_grid_init(raw.data_ptr(), B, gx, gy, H, W, C, init_scale,
+                       image.data_ptr() if image is not None else None, _stream(dev))
+    return raw
+
+
+class GridActivation(torch.autograd.Function):
+    """params = activation(raw) on a gx x gy grid over an H x W frame."""
+
+    @staticmethod
+    def forward(ctx, raw, gx, gy, H, W):
+        raw = raw.contiguous()
+        B, N, P = raw.shape
+        if N != gx * gy or raw.dtype != torch.float32 or P < 6:
+            raise ValueError("raw must be float32 [B, gx*gy, 5 + C]")
+        params = torch.empty_like(raw)
+        _lib.pdr_params_activate(raw.data_ptr(), params.data_ptr(), B, gx, gy, H, W, P - 5,
+                                 _stream(raw.device))
+        ctx.save_for_backward(raw)
+        ctx.meta = (gx, gy, H, W)
+        return params
+
+    @staticmethod
+    def backward(ctx, grad_params):
+        (raw,) = ctx.saved_tensors
+        gx, gy, H, W = ctx.meta
+        g = grad_params.contiguous()
+        out = torch.empty_like(raw)
+        B, N, P = raw.shape
+        _lib.pdr_params_activate_backward(raw.data_ptr(), g.data_ptr(), out.data_ptr(), B, gx, gy,
+                                          H, W, P - 5, _stream(raw.device))
+        return out, None, None, None, None
+
+
+def activate(raw, gx: int, gy: int, H: int, W: int):
+    return GridActivation.apply(raw, gx, gy, H, W)

@@ -113,7 +113,8 @@ enum pdr_kernel_id {
     PDR_K_PREPROCESS = 0, PDR_K_BIN_COUNT = 1, PDR_K_SCAN = 2, PDR_K_BIN_WRITE = 3,
     PDR_K_FORWARD_RASTER = 4, PDR_K_ZERO = 5, PDR_K_BACKWARD_RASTER = 6, PDR_K_FINALIZE = 7,
     PDR_K_LOSS_FWD = 8, PDR_K_LOSS_BWD = 9, PDR_K_LOSS_REDUCE = 10,
-    PDR_KERNEL_COUNT = 11
+    PDR_K_GRID_INIT = 11, PDR_K_ACTIVATE = 12, PDR_K_ACTIVATE_BWD = 13,
+    PDR_KERNEL_COUNT = 14
 };
 int pdr_splat_timing(int enable);
 int pdr_splat_timing_read(double *total_ms, long long *launches, int reset);
@@ -144,6 +145,58 @@ long long pdr_loss_workspace_bytes(int B, int H, int W, int C);
 int pdr_loss_l1_ssim(const float *image, const float *target, int B, int H, int W, int C,
                      float lambda, float c1, float c2, float *grad_image, double *loss,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Concat fusion ("Learning Video Dynamics with Predictive Differentiable
+ * Rendering", reading notes, "Core Idea" and "Relation To Prior Work": the
+ * Gaussian branch's rendered frame is fused with the pixel branch's coarse
+ * prediction by concatenation).  out [B][H][W][Cp + C] receives, per pixel,
+ * the Cp channels of pixel [B][H][W][Cp] followed by the C rendered
+ * channels, written by the forward raster itself (no separate copy or
+ * concat pass).  Cp >= 0; pixel may be NULL only when Cp = 0.  Same
+ * workspace, errors and overflow protocol as pdr_splat_forward. */
+int pdr_splat_forward_concat(const float *params, const float *pixel, int Cp, float *out, int B,
+                             int N, int H, int W, int C, float radius, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Backward of pdr_splat_forward_concat: grad_out [B][H][W][Cp + C]; the last
+ * C channels of every pixel drive the renderer's backward into grad_params
+ * (as pdr_splat_backward), the first Cp are copied to grad_pixel
+ * [B][H][W][Cp] (skipped when grad_pixel is NULL). */
+int pdr_splat_backward_concat(const float *params, const float *grad_out, int Cp,
+                              float *grad_params, float *grad_pixel, int B, int N, int H, int W,
+                              int C, float radius, void *workspace, size_t workspace_bytes,
+                              int reuse_binning, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Adapter-side plain ops (reading notes, "Method": the adapter regresses the
+ * 5 + C parameters per Gaussian from the backbone's coarse prediction;
+ * "Relation To Prior Work": grid initialisation).  The pages give no
+ * formulas; these are the readings:
+ *
+ * Grid: N = gx * gy Gaussians per frame, n = j * gx + i (row-major), cell
+ * cw = W / gx, ch = H / gy, centre ((i + 1/2) cw, (j + 1/2) ch).
+ * Activation of raw adapter values r [B][N][5 + C] into renderer params:
+ *   mu_x = centre_x + cw tanh(r0), mu_y = centre_y + ch tanh(r1),
+ *   s1 = cw exp(r2), s2 = ch exp(r3), theta = r4, a_c = r_{5+c}.
+ * All pointers are device pointers, fp32, contiguous; B*N*(5+C) < 2^31,
+ * N <= 2^22, H, W <= 32767; asynchronous on stream. */
+
+/* raw [B][N][5 + C] = (0, 0, ln s0, ln s0, 0, a): activates to Gaussians on
+ * the grid centres with scales s0 * cell and theta = 0; a_c is image
+ * [B][H][W][C] at the pixel holding the centre, floor((2i + 1) W / (2 gx)),
+ * floor((2j + 1) H / (2 gy)), or 0 when image is NULL.  init_scale = s0 > 0. */
+int pdr_grid_init(float *raw, int B, int gx, int gy, int H, int W, int C, float init_scale,
+                  const float *image, void *stream);
+
+/* params [B][N][5 + C] = activation of raw (same layout; may not alias). */
+int pdr_params_activate(const float *raw, float *params, int B, int gx, int gy, int H, int W,
+                        int C, void *stream);
+
+/* grad_raw = dL/draw from grad_params = dL/dparams (elementwise chain rule
+ * of the activation; grad_raw may alias grad_params). */
+int pdr_params_activate_backward(const float *raw, const float *grad_params, float *grad_raw,
+                                 int B, int gx, int gy, int H, int W, int C, void *stream);
 
 #ifdef __cplusplus
 }

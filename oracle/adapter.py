@@ -48,9 +48,11 @@ def grid_init(B, gx, gy, H, W, C, s0, image=None):
     raw[..., 2] = np.log(s0)
     raw[..., 3] = np.log(s0)
     if image is not None:
-        g, _ = grid_centres(gx, gy, H, W)
-        px = np.minimum(np.floor(g[:, 0]).astype(np.int64), W - 1)
-        py = np.minimum(np.floor(g[:, 1]).astype(np.int64), H - 1)
+        # the pixel containing the centre, floor((2i + 1) W / (2 gx)), in
+        # exact integer arithmetic
+        j, i = np.divmod(np.arange(N), gx)
+        px = ((2 * i + 1) * W) // (2 * gx)
+        py = ((2 * j + 1) * H) // (2 * gy)
         raw[..., 5:] = np.asarray(image, np.float64)[:, py, px, :]
     return raw
 
@@ -74,8 +76,9 @@ def activate_backward(raw, grad_params, gx, gy, H, W):
     gp = np.asarray(grad_params, np.float64)
     _, (cw, ch) = grid_centres(gx, gy, H, W)
     out = np.array(gp, np.float64)
-    out[..., 0] = gp[..., 0] * cw * (1.0 - np.tanh(r[..., 0]) ** 2)
-    out[..., 1] = gp[..., 1] * ch * (1.0 - np.tanh(r[..., 1]) ** 2)
+    # d tanh(r)/dr = sech^2 r, written 1 / cosh^2 r (no cancellation at large |r|)
+    out[..., 0] = gp[..., 0] * cw / np.cosh(r[..., 0]) ** 2
+    out[..., 1] = gp[..., 1] * ch / np.cosh(r[..., 1]) ** 2
     out[..., 2] = gp[..., 2] * cw * np.exp(r[..., 2])
     out[..., 3] = gp[..., 3] * ch * np.exp(r[..., 3])
     return out

@@ -108,7 +108,7 @@ def test_timing_toggle_without_device():
     t = _lib.pdr_splat_timing_read(reset=True)
     assert set(t) == {"preprocess", "bin_count", "scan", "bin_write", "forward_raster",
                       "zero_verify", "backward_raster", "finalize", "loss_fwd", "loss_bwd",
-                      "loss_reduce"}
+                      "loss_reduce", "grid_init", "activate", "activate_bwd"}
     assert all(v == (0.0, 0) for v in t.values())
 
 
@@ -137,3 +137,39 @@ def test_loss_entry_points_validate():
     assert call(c1=0.0) == -1 and call(c2=-1.0) == -1 and call(c2=math.inf) == -1
     assert call(B=0) == -1 and call(C=0) == -1
     assert call(ws=FAKE + 8) == -2 and call(wsb=16) == -2
+
+
+def test_adapter_entry_points_validate():
+    L = _lib.lib()
+    # grid_init(raw, B, gx, gy, H, W, C, s0, image, stream)
+    assert L.pdr_grid_init(None, 1, 4, 4, 16, 16, 3, 0.5, None, None) == -1
+    assert L.pdr_grid_init(FAKE, 0, 4, 4, 16, 16, 3, 0.5, None, None) == -1
+    assert L.pdr_grid_init(FAKE, 1, 0, 4, 16, 16, 3, 0.5, None, None) == -1
+    assert L.pdr_grid_init(FAKE, 1, 4, 4, 16, 16, 0, 0.5, None, None) == -1
+    assert L.pdr_grid_init(FAKE, 1, 4, 4, 16, 16, 3, 0.0, None, None) == -1
+    assert L.pdr_grid_init(FAKE, 1, 4, 4, 16, 16, 3, math.inf, None, None) == -1
+    assert L.pdr_grid_init(FAKE, 1, 4, 4, 40000, 16, 3, 0.5, None, None) == -1
+    assert L.pdr_grid_init(FAKE, 1, 1 << 12, 1 << 11, 16, 16, 3, 0.5, None, None) == -1  # N > 2^22
+    assert L.pdr_grid_init(FAKE, 1 << 10, 1 << 10, 1 << 10, 16, 16, 3, 0.5, None, None) == -1
+    assert L.pdr_params_activate(None, FAKE, 1, 2, 2, 8, 8, 1, None) == -1
+    assert L.pdr_params_activate(FAKE, FAKE, 1, 2, -2, 8, 8, 1, None) == -1
+    assert L.pdr_params_activate_backward(FAKE, None, FAKE, 1, 2, 2, 8, 8, 1, None) == -1
+    assert L.pdr_params_activate_backward(FAKE, FAKE, FAKE, 1, 2, 2, 8, 0, 1, None) == -1
+
+
+def test_concat_entry_points_validate():
+    L = _lib.lib()
+    ws = FAKE
+    # forward_concat(params, pixel, Cp, out, B, N, H, W, C, radius, ws, bytes, stream)
+    assert L.pdr_splat_forward_concat(FAKE, None, 2, FAKE, 1, 4, 8, 8, 1, 3.0, ws, 1 << 20, None) == -1
+    assert L.pdr_splat_forward_concat(FAKE, FAKE, -1, FAKE, 1, 4, 8, 8, 1, 3.0, ws, 1 << 20, None) == -1
+    assert L.pdr_splat_forward_concat(FAKE, FAKE, 2, None, 1, 4, 8, 8, 1, 3.0, ws, 1 << 20, None) == -1
+    assert L.pdr_splat_forward_concat(FAKE, FAKE, 2, FAKE, 1, 4, 8, 8, 1, 0.0, ws, 1 << 20, None) == -1
+    assert L.pdr_splat_forward_concat(FAKE, FAKE, 2, FAKE, 1, 4, 8, 8, 1, 3.0, ws, 16, None) == -2
+    # backward_concat(params, grad_out, Cp, grad_params, grad_pixel, B, N, H, W, C, radius, ...)
+    assert L.pdr_splat_backward_concat(FAKE, FAKE, -3, FAKE, None, 1, 4, 8, 8, 1, 3.0, ws, 1 << 20,
+                                       0, None) == -1
+    assert L.pdr_splat_backward_concat(FAKE, None, 2, FAKE, None, 1, 4, 8, 8, 1, 3.0, ws, 1 << 20,
+                                       0, None) == -1
+    assert L.pdr_splat_backward_concat(FAKE, FAKE, 2, FAKE, None, 1, 4, 8, 8, 1, 3.0, ws + 8,
+                                       1 << 20, 0, None) == -2
