@@ -61,6 +61,71 @@ def loss_flops_bytes(B, H, W, C):
     return {"loss_fwd": (M * (3 + 220 + 20), M * 20), "loss_bwd": (M * (132 + 8), M * 24)}
 
 
+def adapter_leg(args, _lib, torch, B, N, H, W, C, params, image, grad_image, target, ws, ws_bytes,
+                st, step):
+    """Grid initialisation, activation and its gradient on a square grid of N
+    Gaussians per frame, and the concat-fused step ([target | render] with
+    Cp = C) against the plain step; HIP-event timing of every launch."""
+    g = int(round(N ** 0.5))
+    if g * g != N:
+        return None
+    P = 5 + C
+    dev = params.device
+    raw = torch.empty_like(params)
+    act = torch.empty_like(params)
+    graw = torch.empty_like(params)
+    out = torch.empty((B, H, W, 2 * C), dtype=torch.float32, device=dev)
+    gout = torch.cat([grad_image, grad_image], dim=-1).contiguous()
+    gparams = torch.empty_like(params)
+    gpix = torch.empty_like(image)
+
+    def ops():
+        _lib.pdr_grid_init(raw.data_ptr(), B, g, g, H, W, C, 0.5, target.data_ptr(), st)
+        _lib.pdr_params_activate(raw.data_ptr(), act.data_ptr(), B, g, g, H, W, C, st)
+        # (the activated values stand in for dL/dparams)
+        _lib.pdr_params_activate_backward(raw.data_ptr(), act.data_ptr(), graw.data_ptr(), B, g, g,
+                                          H, W, C, st)
+
+    def concat_step():
+        _lib.pdr_splat_forward_concat(params.data_ptr(), target.data_ptr(), C, out.data_ptr(), B,
+                                      N, H, W, C, args.radius, ws.data_ptr(), ws_bytes, st)
+        _lib.pdr_splat_backward_concat(params.data_ptr(), gout.data_ptr(), C, gparams.data_ptr(),
+                                       gpix.data_ptr(), B, N, H, W, C, args.radius, ws.data_ptr(),
+                                       ws_bytes, 1, st)
+
+    for _ in range(args.warmup):
+        ops()
+        concat_step()
+    _lib.pdr_splat_timing(True)
+    _lib.pdr_splat_timing_read(reset=True)
+    for _ in range(args.steps):
+        ops()
+    torch.cuda.synchronize()
+    t = _lib.pdr_splat_timing_read(reset=True)
+    _lib.pdr_splat_timing(False)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"grid": "%dx%d" % (g, g), "kernels": {}}
+    per = B * N * P * 4
+    nbytes = {"grid_init": per + B * N * C * 4, "activate": 2 * per,
+              "activate_bwd": 2 * per + B * N * 4 * 4}
+    for name in ("grid_init", "activate", "activate_bwd"):
+        tot, cnt = t[name]
+        avg = tot / cnt
+        res["kernels"][name] = {"avg_ms": round(avg, 5),
+                                "alg_GBps": round(nbytes[name] / (avg * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(nbytes[name] / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    for name, fn in (("plain_step_ms", step), ("concat_step_ms", concat_step)):
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / args.steps, 5)
+    res["concat_extra_bytes"] = 4 * B * H * W * C * 4   # pixel read + write, gradient read + write
+    return res
+
+
 def source_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -266,6 +331,9 @@ def main():
                             "frac": round(lach / FP32_PEAK_TFLOPS, 4),
                             "hbm_frac": round(loss_out["kernels"][ldom]["alg_GBps"] / HBM_PEAK_GBS, 4)}
 
+    adapter_out = adapter_leg(args, _lib, torch, B, N, H, W, C, params, image, grad_image, target,
+                              ws, ws_bytes, st, step)
+
     cpu, support_pairs = None, None
     if not args.no_cpu_baseline:
         cpu, support_pairs = cpu_baseline_leg(params_np, grad_np, wl, args.radius, args.cpu_budget)
@@ -328,6 +396,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "loss": loss_out,
+        "adapter": adapter_out,
     }
     print(json.dumps(out), flush=True)
 

@@ -165,6 +165,7 @@ int pdr_grid_init(float *raw, int B, int gx, int gy, int H, int W, int C, float 
 int pdr_params_activate(const float *raw, float *params, int B, int gx, int gy, int H, int W,
                         int C, void *stream) {
   if (!raw || !params) return PDR_ERR_INVALID_ARG;
+  if (((uintptr_t)raw | (uintptr_t)params) & 15u) return PDR_ERR_INVALID_ARG;
   int rc = validate_grid(B, gx, gy, H, W, C);
   if (rc != PDR_OK) return rc;
   return hip_status(launch_activate(raw, params, B, gx, gy, H, W, C, (hipStream_t)stream));
@@ -173,6 +174,8 @@ int pdr_params_activate(const float *raw, float *params, int B, int gx, int gy, 
 int pdr_params_activate_backward(const float *raw, const float *grad_params, float *grad_raw,
                                  int B, int gx, int gy, int H, int W, int C, void *stream) {
   if (!raw || !grad_params || !grad_raw) return PDR_ERR_INVALID_ARG;
+  if (((uintptr_t)raw | (uintptr_t)grad_params | (uintptr_t)grad_raw) & 15u)
+    return PDR_ERR_INVALID_ARG;
   int rc = validate_grid(B, gx, gy, H, W, C);
   if (rc != PDR_OK) return rc;
   return hip_status(launch_activate_backward(raw, grad_params, grad_raw, B, gx, gy, H, W, C,

@@ -14,9 +14,10 @@
 // Grid initialisation writes r = (0, 0, ln s0, ln s0, 0, a), a sampled from
 // an optional coarse frame at the pixel holding the centre (else 0).
 //
-// All three are elementwise over the B*N*(5+C) values (HBM-bound): one
-// thread per value, coalesced, with the value's (Gaussian, slot) found by
-// multiply-shift division by the invariant row length.
+// All three are elementwise over the B*N*(5+C) values (HBM-bound),
+// coalesced, with the value's (Gaussian, slot) found by multiply-shift
+// division by the invariant row length; the activation and its gradient move
+// four values per thread with 16-byte accesses (buffers 16-byte aligned).
 #include <math.h>
 #include <stdint.h>
 
@@ -79,31 +80,71 @@ __global__ __launch_bounds__(kElemThreads) void k_grid_init(float *__restrict__ 
     v = log_s0;
   } else if (k >= 5 && image) {
     const uint32_t j = fdiv(n, g.gx), i = n - j * g.gx.d;
-    // the pixel holding the centre: floor((2i + 1) W / (2 gx)), exactly
-    const int px = (int)(((2ull * i + 1ull) * (uint64_t)g.W) / (2ull * g.gx.d));
-    const int py = (int)(((2ull * j + 1ull) * (uint64_t)g.H) / (2ull * (uint64_t)g.gy));
+    // the pixel holding the centre, floor((2i + 1) W / (2 gx)): the fp64
+    // quotient of these integers (< 2^40) is within 4e-12 of the exact one,
+    // which is either an integer (then exact) or at least 1/(2 gx) > 1e-7
+    // from the next one, so its floor is exact
+    const int px = (int)floor((double)(2u * i + 1u) * (double)g.W / (2.0 * (double)g.gx.d));
+    const int py = (int)floor((double)(2u * j + 1u) * (double)g.H / (2.0 * (double)g.gy));
     v = image[(((size_t)b * g.H + py) * g.W + px) * (size_t)g.C + (k - 5)];
   }
   raw[e] = v;
 }
 
+// The activation of value e = (Gaussian gi, slot k), gi = b * N + n.
+__device__ __forceinline__ float act_value(float r, uint32_t n, uint32_t k, const GridArgs &g) {
+  if (k >= 4) return r;
+  const uint32_t j = fdiv(n, g.gx), i = n - j * g.gx.d;
+  if (k == 0) return (float)(((double)i + 0.5) * g.cw + g.cw * (double)tanhf(r));
+  if (k == 1) return (float)(((double)j + 0.5) * g.ch + g.ch * (double)tanhf(r));
+  const float e = expf(r);
+  return (float)((k == 2 ? g.cw : g.ch) * (double)e);
+}
+
+// Its derivative applied to dL/dparams gp.
+__device__ __forceinline__ float act_grad(float gp, float r, uint32_t k, const GridArgs &g) {
+  if (k >= 4) return gp;
+  const float cell = (float)((k & 1) ? g.ch : g.cw);
+  if (k < 2) {
+    // d tanh / dr = sech^2 r = 1 / cosh^2 r (1 - tanh^2 r would cancel at large |r|)
+    const float c = coshf(r);
+    return gp * (cell / (c * c));
+  }
+  return gp * (cell * expf(r));
+}
+
+// Four consecutive values per thread (16-byte loads and stores); the slot
+// and grid index advance with wrap-around from the first one.
 __global__ __launch_bounds__(kElemThreads) void k_activate(const float *__restrict__ raw,
                                                           float *__restrict__ params,
                                                           uint32_t total, GridArgs g) {
-  const uint32_t e = blockIdx.x * kElemThreads + threadIdx.x;
-  if (e >= total) return;
-  uint32_t b, n, k;
-  locate(e, g, &b, &n, &k);
-  const float r = raw[e];
-  float v = r;
-  if (k < 4) {
-    const uint32_t j = fdiv(n, g.gx), i = n - j * g.gx.d;
-    if (k == 0) v = (float)(((double)i + 0.5) * g.cw + g.cw * (double)tanhf(r));
-    else if (k == 1) v = (float)(((double)j + 0.5) * g.ch + g.ch * (double)tanhf(r));
-    else if (k == 2) v = (float)(g.cw * (double)expf(r));
-    else v = (float)(g.ch * (double)expf(r));
+  const uint32_t t = blockIdx.x * kElemThreads + threadIdx.x;
+  const uint32_t e0 = 4u * t;
+  if (e0 >= total) return;
+  const uint32_t gi = fdiv(e0, g.row);
+  uint32_t k = e0 - gi * g.row.d;
+  uint32_t n = gi - fdiv(gi, g.nper) * g.nper.d;
+  if (e0 + 4u <= total) {
+    const float4 r = reinterpret_cast<const float4 *>(raw)[t];
+    float v[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = act_value(v[q], n, k, g);
+      if (++k == g.row.d) {
+        k = 0;
+        if (++n == g.nper.d) n = 0;
+      }
+    }
+    reinterpret_cast<float4 *>(params)[t] = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    for (uint32_t e = e0; e < total; ++e) {
+      params[e] = act_value(raw[e], n, k, g);
+      if (++k == g.row.d) {
+        k = 0;
+        if (++n == g.nper.d) n = 0;
+      }
+    }
   }
-  params[e] = v;
 }
 
 // gparams and graw may be the same buffer (each value is read, then written,
@@ -111,22 +152,27 @@ __global__ __launch_bounds__(kElemThreads) void k_activate(const float *__restri
 __global__ __launch_bounds__(kElemThreads) void k_activate_bwd(const float *__restrict__ raw,
                                                               const float *gparams, float *graw,
                                                               uint32_t total, GridArgs g) {
-  const uint32_t e = blockIdx.x * kElemThreads + threadIdx.x;
-  if (e >= total) return;
-  const uint32_t k = e - fdiv(e, g.row) * g.row.d;
-  const float gp = gparams[e];
-  float v = gp;
-  if (k < 4) {
-    const float r = raw[e];
-    if (k < 2) {
-      // d tanh / dr = sech^2 r = 1 / cosh^2 r (1 - tanh^2 r would cancel at large |r|)
-      const double c = (double)coshf(r);
-      v = (float)((double)gp * (k == 0 ? g.cw : g.ch) / (c * c));
-    } else {
-      v = (float)((double)gp * (k == 2 ? g.cw : g.ch) * (double)expf(r));
+  const uint32_t t = blockIdx.x * kElemThreads + threadIdx.x;
+  const uint32_t e0 = 4u * t;
+  if (e0 >= total) return;
+  uint32_t k = e0 - fdiv(e0, g.row) * g.row.d;
+  if (e0 + 4u <= total) {
+    const float4 gp = reinterpret_cast<const float4 *>(gparams)[t];
+    const float4 r = reinterpret_cast<const float4 *>(raw)[t];
+    float v[4] = {gp.x, gp.y, gp.z, gp.w};
+    const float rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = act_grad(v[q], rr[q], k, g);
+      if (++k == g.row.d) k = 0;
+    }
+    reinterpret_cast<float4 *>(graw)[t] = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    for (uint32_t e = e0; e < total; ++e) {
+      graw[e] = act_grad(gparams[e], raw[e], k, g);
+      if (++k == g.row.d) k = 0;
     }
   }
-  graw[e] = v;
 }
 
 GridArgs grid_args(int B, int gx, int gy, int H, int W, int C) {
@@ -161,8 +207,9 @@ hipError_t launch_activate(const float *raw, float *params, int B, int gx, int g
                            int C, hipStream_t st) {
   const GridArgs g = grid_args(B, gx, gy, H, W, C);
   const uint32_t total = (uint32_t)((long long)B * gx * gy * (5 + C));
+  const uint32_t threads = (total + 3u) / 4u;
   PDR_TIMED(PDR_K_ACTIVATE, st,
-            hipLaunchKernelGGL(k_activate, dim3((total + kElemThreads - 1) / kElemThreads),
+            hipLaunchKernelGGL(k_activate, dim3((threads + kElemThreads - 1) / kElemThreads),
                                dim3(kElemThreads), 0, st, raw, params, total, g));
   return hipGetLastError();
 }
@@ -171,8 +218,9 @@ hipError_t launch_activate_backward(const float *raw, const float *grad_params, 
                                     int B, int gx, int gy, int H, int W, int C, hipStream_t st) {
   const GridArgs g = grid_args(B, gx, gy, H, W, C);
   const uint32_t total = (uint32_t)((long long)B * gx * gy * (5 + C));
+  const uint32_t threads = (total + 3u) / 4u;
   PDR_TIMED(PDR_K_ACTIVATE_BWD, st,
-            hipLaunchKernelGGL(k_activate_bwd, dim3((total + kElemThreads - 1) / kElemThreads),
+            hipLaunchKernelGGL(k_activate_bwd, dim3((threads + kElemThreads - 1) / kElemThreads),
                                dim3(kElemThreads), 0, st, raw, grad_params, grad_raw, total, g));
   return hipGetLastError();
 }

@@ -189,12 +189,14 @@ int pdr_splat_backward_concat(const float *params, const float *grad_out, int Cp
 int pdr_grid_init(float *raw, int B, int gx, int gy, int H, int W, int C, float init_scale,
                   const float *image, void *stream);
 
-/* params [B][N][5 + C] = activation of raw (same layout; may not alias). */
+/* params [B][N][5 + C] = activation of raw (same layout; may not alias).
+ * raw and params 16-byte aligned (PDR_ERR_INVALID_ARG otherwise). */
 int pdr_params_activate(const float *raw, float *params, int B, int gx, int gy, int H, int W,
                         int C, void *stream);
 
 /* grad_raw = dL/draw from grad_params = dL/dparams (elementwise chain rule
- * of the activation; grad_raw may alias grad_params). */
+ * of the activation; grad_raw may alias grad_params).  All three pointers
+ * 16-byte aligned (PDR_ERR_INVALID_ARG otherwise). */
 int pdr_params_activate_backward(const float *raw, const float *grad_params, float *grad_raw,
                                  int B, int gx, int gy, int H, int W, int C, void *stream);
 

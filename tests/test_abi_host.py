@@ -155,6 +155,8 @@ def test_adapter_entry_points_validate():
     assert L.pdr_params_activate(FAKE, FAKE, 1, 2, -2, 8, 8, 1, None) == -1
     assert L.pdr_params_activate_backward(FAKE, None, FAKE, 1, 2, 2, 8, 8, 1, None) == -1
     assert L.pdr_params_activate_backward(FAKE, FAKE, FAKE, 1, 2, 2, 8, 0, 1, None) == -1
+    assert L.pdr_params_activate(FAKE + 4, FAKE, 1, 2, 2, 8, 8, 1, None) == -1      # 16-B alignment
+    assert L.pdr_params_activate_backward(FAKE, FAKE, FAKE + 8, 1, 2, 2, 8, 8, 1, None) == -1
 
 
 def test_concat_entry_points_validate():
