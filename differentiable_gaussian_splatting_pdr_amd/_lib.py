@@ -38,6 +38,8 @@ EXPORTED = (
     "pdr_grid_init",
     "pdr_params_activate",
     "pdr_params_activate_backward",
+    "pdr_splat_forward_fmt",
+    "pdr_splat_backward_fmt",
 )
 
 KERNEL_COUNT = 14
@@ -96,6 +98,10 @@ def lib() -> ctypes.CDLL:
         L.pdr_params_activate.restype = i
         L.pdr_params_activate_backward.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
         L.pdr_params_activate_backward.restype = i
+        L.pdr_splat_forward_fmt.argtypes = [vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        L.pdr_splat_forward_fmt.restype = i
+        L.pdr_splat_backward_fmt.argtypes = [vp, vp, i, vp, i, i, i, i, i, f, vp, sz, i, vp]
+        L.pdr_splat_backward_fmt.restype = i
         _lib = L
     return _lib
 
@@ -201,3 +207,21 @@ def pdr_params_activate_backward(raw, grad_params, grad_raw, B, gx, gy, H, W, C,
     return _raise(lib().pdr_params_activate_backward(raw, grad_params, grad_raw, B, gx, gy, H, W,
                                                      C, stream),
                   "pdr_params_activate_backward")
+
+
+PDR_FMT_F32, PDR_FMT_F16, PDR_FMT_BF16 = 0, 1, 2
+
+
+def pdr_splat_forward_fmt(params, image, image_format, B, N, H, W, C, radius, workspace,
+                          workspace_bytes, stream):
+    return _raise(lib().pdr_splat_forward_fmt(params, image, int(image_format), B, N, H, W, C,
+                                              float(radius), workspace, workspace_bytes, stream),
+                  "pdr_splat_forward_fmt")
+
+
+def pdr_splat_backward_fmt(params, grad_image, grad_format, grad_params, B, N, H, W, C, radius,
+                           workspace, workspace_bytes, reuse_binning, stream):
+    return _raise(lib().pdr_splat_backward_fmt(params, grad_image, int(grad_format), grad_params,
+                                               B, N, H, W, C, float(radius), workspace,
+                                               workspace_bytes, int(reuse_binning), stream),
+                  "pdr_splat_backward_fmt")

@@ -55,12 +55,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PDR_OK : PDR_ERR_HIP; }
 
 // Forward (binning + raster) into image with Cp leading pixel-branch
 // channels per pixel (Cp = 0: the plain layout).
-int forward_impl(const float *params, const float *pixel, int Cp, float *image, int B, int N,
+int forward_impl(const float *params, const float *pixel, int Cp, void *image, int B, int N,
                  int H, int W, int C, float radius, void *workspace, size_t workspace_bytes,
-                 void *stream) {
+                 void *stream, int fmt = PDR_FMT_F32) {
   Dims d;
   Layout L;
   if (!params || !image) return PDR_ERR_INVALID_ARG;
+  if (fmt != PDR_FMT_F32 && fmt != PDR_FMT_F16 && fmt != PDR_FMT_BF16) return PDR_ERR_INVALID_ARG;
   int rc = validate_sizes(B, N, H, W, C, &d);
   if (rc == PDR_OK) rc = validate_radius(radius);
   if (rc == PDR_OK && (long long)B * H * W * (Cp + (long long)C) > (1LL << 46)) rc = PDR_ERR_INVALID_ARG;
@@ -71,16 +72,19 @@ int forward_impl(const float *params, const float *pixel, int Cp, float *image, 
   hipError_t e = launch_binning(params, B, N, H, W, C, radius, workspace, L, (int *)(w + L.tile_off),
                                 (int *)(w + L.list), L.cap, true, st);
   if (e == hipSuccess)
-    e = launch_forward_raster(params, image, B, N, H, W, C, radius, workspace, L, st, pixel, Cp);
+    e = launch_forward_raster(params, image, B, N, H, W, C, radius, workspace, L, st, pixel, Cp,
+                              fmt);
   return hip_status(e);
 }
 
-int backward_impl(const float *params, const float *grad_image, int Cp, float *grad_params,
+int backward_impl(const float *params, const void *grad_image, int Cp, float *grad_params,
                   float *grad_pixel, int B, int N, int H, int W, int C, float radius,
-                  void *workspace, size_t workspace_bytes, int reuse_binning, void *stream) {
+                  void *workspace, size_t workspace_bytes, int reuse_binning, void *stream,
+                  int fmt = PDR_FMT_F32) {
   Dims d;
   Layout L;
   if (!params || !grad_image || !grad_params) return PDR_ERR_INVALID_ARG;
+  if (fmt != PDR_FMT_F32 && fmt != PDR_FMT_F16 && fmt != PDR_FMT_BF16) return PDR_ERR_INVALID_ARG;
   int rc = validate_sizes(B, N, H, W, C, &d);
   if (rc == PDR_OK) rc = validate_radius(radius);
   if (rc == PDR_OK && (long long)B * H * W * (Cp + (long long)C) > (1LL << 46)) rc = PDR_ERR_INVALID_ARG;
@@ -94,7 +98,7 @@ int backward_impl(const float *params, const float *grad_image, int Cp, float *g
                        (int *)(w + L.list), L.cap, true, st);
   if (e == hipSuccess)
     e = launch_backward(params, grad_image, grad_params, B, N, H, W, C, radius, workspace, L,
-                        reuse_binning != 0, st, grad_pixel, Cp);
+                        reuse_binning != 0, st, grad_pixel, Cp, fmt);
   return hip_status(e);
 }
 
@@ -133,6 +137,21 @@ int pdr_splat_backward(const float *params, const float *grad_image, float *grad
                        size_t workspace_bytes, int reuse_binning, void *stream) {
   return backward_impl(params, grad_image, 0, grad_params, nullptr, B, N, H, W, C, radius,
                        workspace, workspace_bytes, reuse_binning, stream);
+}
+
+int pdr_splat_forward_fmt(const float *params, void *image, int image_format, int B, int N, int H,
+                          int W, int C, float radius, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  return forward_impl(params, nullptr, 0, image, B, N, H, W, C, radius, workspace, workspace_bytes,
+                      stream, image_format);
+}
+
+int pdr_splat_backward_fmt(const float *params, const void *grad_image, int grad_format,
+                           float *grad_params, int B, int N, int H, int W, int C, float radius,
+                           void *workspace, size_t workspace_bytes, int reuse_binning,
+                           void *stream) {
+  return backward_impl(params, grad_image, 0, grad_params, nullptr, B, N, H, W, C, radius,
+                       workspace, workspace_bytes, reuse_binning, stream, grad_format);
 }
 
 int pdr_splat_forward_concat(const float *params, const float *pixel, int Cp, float *out, int B,

@@ -32,19 +32,20 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
 // Forward raster: image[b][y][x][c] for all channels.  With Cp > 0 the
 // output has Cp + C channels per pixel: pixel[b][y][x][0..Cp) first, then the
 // rendered channels (concat fusion).
-hipError_t launch_forward_raster(const float *params, float *image, int B, int N, int H, int W,
+// fmt: PDR_FMT_F32 / F16 / BF16 storage of image (concat needs F32).
+hipError_t launch_forward_raster(const float *params, void *image, int B, int N, int H, int W,
                                  int C, float radius, void *ws, const Layout &L, hipStream_t st,
-                                 const float *pixel = nullptr, int Cp = 0);
+                                 const float *pixel = nullptr, int Cp = 0, int fmt = PDR_FMT_F32);
 
 // Backward: zero grad_params (and verify the binning stamp when reusing),
 // raster the per-Gaussian sums with one atomic per wave per Gaussian, then
 // turn the sums into gradients in place.
 // With Cp > 0, grad_image has Cp + C channels per pixel; the first Cp are
 // copied to grad_pixel (if not null), the rest drive the renderer.
-hipError_t launch_backward(const float *params, const float *grad_image, float *grad_params, int B,
+hipError_t launch_backward(const float *params, const void *grad_image, float *grad_params, int B,
                            int N, int H, int W, int C, float radius, void *ws, const Layout &L,
                            bool check_stamp, hipStream_t st, float *grad_pixel = nullptr,
-                           int Cp = 0);
+                           int Cp = 0, int fmt = PDR_FMT_F32);
 
 // L1 + SSIM loss: grad = dloss/dimage, *loss on the device.
 hipError_t launch_loss(const float *img, const float *tgt, int B, int H, int W, int C, float lam,

@@ -102,18 +102,37 @@ __device__ __forceinline__ void stage_entry(Entry<CP> *s, const GRec *__restrict
 // at pixel * ldo + ooff + c.  With concat fusion (ldo = Cp + C, ooff = Cp)
 // the first Cp channels of every pixel belong to the pixel branch: the
 // forward copies them from xin, the backward copies their gradient to xout.
+// fmt selects the image's storage: fp32, or fp16 / bf16 (round to nearest
+// even from the fp32 accumulators; fp32 arithmetic throughout).
 struct ImgView {
   int ldo, ooff;
   const float *xin;
   float *xout;
   int Cp;
+  int fmt;
 };
+
+__device__ __forceinline__ void store_image(void *base, size_t idx, float v, int fmt) {
+  if (fmt == PDR_FMT_F32) {
+    static_cast<float *>(base)[idx] = v;
+  } else if (fmt == PDR_FMT_F16) {
+    static_cast<_Float16 *>(base)[idx] = (_Float16)v;
+  } else {
+    static_cast<__bf16 *>(base)[idx] = (__bf16)v;
+  }
+}
+
+__device__ __forceinline__ float load_image(const void *base, size_t idx, int fmt) {
+  if (fmt == PDR_FMT_F32) return static_cast<const float *>(base)[idx];
+  if (fmt == PDR_FMT_F16) return (float)static_cast<const _Float16 *>(base)[idx];
+  return (float)static_cast<const __bf16 *>(base)[idx];
+}
 
 template <int CP, int UW, int UX, int UY>
 __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
     const GRec *__restrict__ recs, const float *__restrict__ params,
     const int *__restrict__ tile_off, const int *__restrict__ list, int B, int N, int H, int W,
-    int C, int c0, int cc, float thr, int nTx, int nT, float *__restrict__ image, ImgView iv,
+    int C, int c0, int cc, float thr, int nTx, int nT, void *__restrict__ image, ImgView iv,
     const WsHeader *hdr) {
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
@@ -179,13 +198,13 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
       const int px = rx0 + UW * i + lx, py = ry0 + UH * j + ly;
       if (px < W && py < H) {
         const size_t pix = ((size_t)f * H + py) * W + px;
-        float *o = image + pix * (size_t)iv.ldo + iv.ooff + c0;
+        const size_t o = pix * (size_t)iv.ldo + iv.ooff + c0;
 #pragma unroll
         for (int c = 0; c < CP; ++c)
-          if (c < cc) o[c] = acc[j][i][c];
+          if (c < cc) store_image(image, o + c, acc[j][i][c], iv.fmt);
         if (iv.xin) {   // concat fusion: the pixel branch's channels go first
           const float *xi = iv.xin + pix * (size_t)iv.Cp;
-          float *ob = image + pix * (size_t)iv.ldo;
+          float *ob = static_cast<float *>(image) + pix * (size_t)iv.ldo;   // fp32 only
           for (int c = 0; c < iv.Cp; ++c) ob[c] = xi[c];
         }
       }
@@ -239,7 +258,7 @@ struct Pow2Up {
 template <int CP, int UW, int UX, int UY>
 __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward(
     const GRec *__restrict__ recs, const float *__restrict__ params,
-    const float *__restrict__ gimg, const int *__restrict__ tile_off,
+    const void *__restrict__ gimg, const int *__restrict__ tile_off,
     const int *__restrict__ list, int B, int N, int H, int W, int C, int c0, int cc, float thr,
     int nTx, int nT, float *__restrict__ sums, ImgView iv, const WsHeader *hdr) {
   using WL = WaveLayout<UW, UX, UY>;
@@ -269,11 +288,11 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
       const int px = rx0 + UW * i + lx, py = ry0 + UH * j + ly;
       const bool in = px < W && py < H;
       const size_t pix = ((size_t)f * H + (in ? py : 0)) * W + (in ? px : 0);
-      const float *g = gimg + pix * (size_t)iv.ldo + iv.ooff + c0;
+      const size_t g = pix * (size_t)iv.ldo + iv.ooff + c0;
 #pragma unroll
-      for (int c = 0; c < CP; ++c) G[j][i][c] = (in && c < cc) ? g[c] : 0.f;
-      if (iv.xout && in) {   // concat fusion: the pixel branch's gradient slice
-        const float *gb = gimg + pix * (size_t)iv.ldo;
+      for (int c = 0; c < CP; ++c) G[j][i][c] = (in && c < cc) ? load_image(gimg, g + c, iv.fmt) : 0.f;
+      if (iv.xout && in) {   // concat fusion: the pixel branch's gradient slice (fp32 only)
+        const float *gb = static_cast<const float *>(gimg) + pix * (size_t)iv.ldo;
         float *xo = iv.xout + pix * (size_t)iv.Cp;
         for (int c = 0; c < iv.Cp; ++c) xo[c] = gb[c];
       }
@@ -405,13 +424,13 @@ namespace {
 struct RasterArgs {
   const GRec *recs;
   const float *params;
-  const float *gimg;
+  const void *gimg;
   const int *tile_off;
   const int *list;
   int B, N, H, W, C, c0, cc;
   float thr;
   int nTx, nT;
-  float *out;
+  void *out;
   ImgView iv;
   const WsHeader *hdr;
 };
@@ -433,7 +452,8 @@ void bwd_cp(const RasterArgs &a, hipStream_t st) {
   PDR_TIMED(PDR_K_BACKWARD_RASTER, st,
             hipLaunchKernelGGL((k_backward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
                                a.recs, a.params, a.gimg, a.tile_off, a.list, a.B, a.N, a.H, a.W,
-                               a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr));
+                               a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, static_cast<float *>(a.out),
+                               a.iv, a.hdr));
 }
 
 // Unit shape and units per wave (compile-time tuning knob): 8x8 quads,
@@ -483,19 +503,19 @@ RasterArgs raster_args(const float *params, int B, int N, int H, int W, int C, f
   a.nTx = (W + kTileW - 1) / kTileW;
   a.nT = a.nTx * ((H + kTileH - 1) / kTileH);
   a.out = nullptr;
-  a.iv = ImgView{C, 0, nullptr, nullptr, 0};
+  a.iv = ImgView{C, 0, nullptr, nullptr, 0, PDR_FMT_F32};
   a.hdr = (const WsHeader *)(w + L.hdr);
   return a;
 }
 
 }  // namespace
 
-hipError_t launch_forward_raster(const float *params, float *image, int B, int N, int H, int W,
+hipError_t launch_forward_raster(const float *params, void *image, int B, int N, int H, int W,
                                  int C, float radius, void *ws, const Layout &L, hipStream_t st,
-                                 const float *pixel, int Cp) {
+                                 const float *pixel, int Cp, int fmt) {
   RasterArgs a = raster_args(params, B, N, H, W, C, radius, ws, L);
   a.out = image;
-  a.iv = ImgView{Cp + C, Cp, nullptr, nullptr, Cp};
+  a.iv = ImgView{Cp + C, Cp, nullptr, nullptr, Cp, fmt};
   for (int c0 = 0; c0 < C; c0 += 16) {
     a.c0 = c0;
     a.cc = C - c0 < 16 ? C - c0 : 16;
@@ -505,11 +525,11 @@ hipError_t launch_forward_raster(const float *params, float *image, int B, int N
   return hipGetLastError();
 }
 
-hipError_t launch_backward(const float *params, const float *grad_image, float *grad_params, int B,
+hipError_t launch_backward(const float *params, const void *grad_image, float *grad_params, int B,
                            int N, int H, int W, int C, float radius, void *ws, const Layout &L,
-                           bool check_stamp, hipStream_t st, float *grad_pixel, int Cp) {
+                           bool check_stamp, hipStream_t st, float *grad_pixel, int Cp, int fmt) {
   RasterArgs a = raster_args(params, B, N, H, W, C, radius, ws, L);
-  a.iv = ImgView{Cp + C, Cp, nullptr, nullptr, Cp};
+  a.iv = ImgView{Cp + C, Cp, nullptr, nullptr, Cp, fmt};
   WsHeader *hdr = (WsHeader *)((char *)ws + L.hdr);
   long long BN = (long long)B * N, total = BN * (5 + C);
   long long zb = (total + 255) / 256;

@@ -62,20 +62,31 @@ def _initial_pairs(B, N, H, W) -> int:
     return min(B * N * min(8, ntiles), 0x7FFFFFFF)
 
 
+_FMT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
 def forward(params: torch.Tensor, H: int, W: int, radius: float = 3.0,
-            workspace: Workspace | None = None, image: torch.Tensor | None = None):
+            workspace: Workspace | None = None, image: torch.Tensor | None = None,
+            dtype: torch.dtype = torch.float32):
     """Render; returns (image, workspace).  Synchronises once to check the
-    list capacity and re-runs with an exactly sized workspace on overflow."""
+    list capacity and re-runs with an exactly sized workspace on overflow.
+    dtype float16 / bfloat16 stores the image in that format (fp32 math)."""
     B, N, C = _check_params(params)
     dev = params.device
     ws = workspace or Workspace(dev)
     ws.ensure(Workspace.bytes_for(B, N, H, W, C, _initial_pairs(B, N, H, W)))
     if image is None:
-        image = torch.empty((B, H, W, C), dtype=torch.float32, device=dev)
+        image = torch.empty((B, H, W, C), dtype=dtype, device=dev)
+    if image.dtype not in _FMT or image.shape != (B, H, W, C) or not image.is_contiguous():
+        raise ValueError("image must be contiguous [B, H, W, C] float32/float16/bfloat16")
     st = _stream(dev)
     for _ in range(2):
-        _lib.pdr_splat_forward(params.data_ptr(), image.data_ptr(), B, N, H, W, C, radius,
-                               ws.ptr, ws.nbytes, st)
+        if image.dtype == torch.float32:
+            _lib.pdr_splat_forward(params.data_ptr(), image.data_ptr(), B, N, H, W, C, radius,
+                                   ws.ptr, ws.nbytes, st)
+        else:
+            _lib.pdr_splat_forward_fmt(params.data_ptr(), image.data_ptr(), _FMT[image.dtype], B,
+                                       N, H, W, C, radius, ws.ptr, ws.nbytes, st)
         rc, need = _lib.pdr_splat_check(ws.ptr, st)
         if rc == _lib.PDR_OK:
             return image, ws
@@ -92,8 +103,8 @@ def backward(params: torch.Tensor, grad_image: torch.Tensor, H: int, W: int,
     """dL/dparams for dL/dimage; returns grad_params."""
     B, N, C = _check_params(params)
     dev = params.device
-    if grad_image.shape != (B, H, W, C) or grad_image.dtype != torch.float32:
-        raise ValueError("grad_image must be float32 [B, H, W, C]")
+    if grad_image.shape != (B, H, W, C) or grad_image.dtype not in _FMT:
+        raise ValueError("grad_image must be [B, H, W, C] float32/float16/bfloat16")
     grad_image = grad_image.contiguous()
     if grad_params is None:
         grad_params = torch.empty_like(params)
@@ -102,9 +113,15 @@ def backward(params: torch.Tensor, grad_image: torch.Tensor, H: int, W: int,
         reuse_binning = False
         workspace = Workspace(dev, Workspace.bytes_for(B, N, H, W, C, _initial_pairs(B, N, H, W)))
     for _ in range(2):
-        _lib.pdr_splat_backward(params.data_ptr(), grad_image.data_ptr(), grad_params.data_ptr(),
-                                B, N, H, W, C, radius, workspace.ptr, workspace.nbytes,
-                                int(reuse_binning), st)
+        if grad_image.dtype == torch.float32:
+            _lib.pdr_splat_backward(params.data_ptr(), grad_image.data_ptr(),
+                                    grad_params.data_ptr(), B, N, H, W, C, radius, workspace.ptr,
+                                    workspace.nbytes, int(reuse_binning), st)
+        else:
+            _lib.pdr_splat_backward_fmt(params.data_ptr(), grad_image.data_ptr(),
+                                        _FMT[grad_image.dtype], grad_params.data_ptr(), B, N, H,
+                                        W, C, radius, workspace.ptr, workspace.nbytes,
+                                        int(reuse_binning), st)
         if not check:
             return grad_params
         rc, need = _lib.pdr_splat_check(workspace.ptr, st)

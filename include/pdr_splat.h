@@ -147,6 +147,26 @@ int pdr_loss_l1_ssim(const float *image, const float *target, int B, int H, int 
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Reduced-precision image storage (page 3 of the sources, first paragraph,
+ * evaluates FP16 rendering targets for splatting).  The renderer computes
+ * and accumulates in fp32 exactly as pdr_splat_forward / _backward; only
+ * the image it writes, or the dL/dimage it reads, is stored as fp16 or bf16
+ * (IEEE binary16 / bfloat16, round to nearest even), halving those
+ * tensors' bytes.  Same layouts, errors and workspace protocol. */
+typedef enum { PDR_FMT_F32 = 0, PDR_FMT_F16 = 1, PDR_FMT_BF16 = 2 } pdr_format;
+
+/* image [B][H][W][C] of the given format (2 or 4 bytes per value). */
+int pdr_splat_forward_fmt(const float *params, void *image, int image_format, int B, int N, int H,
+                          int W, int C, float radius, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* grad_image [B][H][W][C] of the given format; grad_params fp32. */
+int pdr_splat_backward_fmt(const float *params, const void *grad_image, int grad_format,
+                           float *grad_params, int B, int N, int H, int W, int C, float radius,
+                           void *workspace, size_t workspace_bytes, int reuse_binning,
+                           void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Concat fusion ("Learning Video Dynamics with Predictive Differentiable
  * Rendering", reading notes, "Core Idea" and "Relation To Prior Work": the
  * Gaussian branch's rendered frame is fused with the pixel branch's coarse

@@ -90,3 +90,23 @@ def check_lists(orc, params, H, W, radius=3.0, gpu=None):
     assert np.array_equal(off_g, off), "tile offsets differ"
     assert np.array_equal(lst_g, lst), "tile lists differ"
     return int(off[-1])
+
+
+def quantize(x, fmt):
+    """Round float32 values to the storage format (round to nearest even) and
+    return them as float32; fmt 'f16' or 'bf16'."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if fmt == "f16":
+        return x.astype(np.float16).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16          # bfloat16: keep the top 16 bits, RNE
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+def format_spacing(ref, fmt):
+    """Distance between adjacent values of the format around |ref| (float64)."""
+    a = np.abs(np.asarray(ref, np.float64))
+    if fmt == "f16":
+        return np.spacing(a.astype(np.float16)).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)

@@ -1,0 +1,63 @@
+"""Reduced-precision image storage (fp16 / bf16) against the fp64 oracle.
+
+The renderer computes in fp32 either way; only the image it writes (or the
+dL/dI it reads) is rounded to the format.  Forward bound: one spacing of the
+format at |ref| (round-to-nearest of a value that is itself within the fp32
+tolerance) plus the fp32 tolerance.  Backward: dL/dI is rounded to the
+format on the host first, the oracle takes the same rounded values, and the
+fp32 gradient tolerance applies unchanged."""
+import numpy as np
+import pytest
+
+from differentiable_gaussian_splatting_pdr_amd import workloads
+from helpers import check_close, format_spacing, quantize
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": "float16", "bf16": "bfloat16"}
+
+
+def run(params, G, H, W, fmt):
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import splat
+    dev = torch.device("cuda:0")
+    dt = getattr(torch, DT[fmt])
+    p = torch.from_numpy(params).to(dev)
+    img, ws = splat.forward(p, H, W, dtype=dt)
+    gq = torch.from_numpy(quantize(G, fmt)).to(dev).to(dt)
+    gp = splat.backward(p, gq, H, W, workspace=ws, reuse_binning=True)
+    torch.cuda.synchronize()
+    return img.float().cpu().numpy(), gp.cpu().numpy()
+
+
+def check(orc, params, G, H, W, fmt, frames=None):
+    img, gp = run(params, G, H, W, fmt)
+    sel = slice(None) if frames is None else frames
+    ref, slk, _, _ = orc.render(params[sel], H, W, 3.0)
+    check_close(img[sel], ref, np.abs(ref), slk + format_spacing(ref, fmt), "image " + fmt)
+    gr, gsl, gmag = orc.grad(params[sel], quantize(G[sel], fmt), H, W, 3.0)
+    check_close(gp[sel], gr, gmag, gsl, "grad " + fmt)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("case", [
+    dict(B=2, N=50, H=37, W=53, C=3), dict(B=1, N=80, H=40, W=70, C=20), dict(B=3, N=30, H=16, W=16, C=1),
+])
+def test_reduced_precision_small(orc, fmt, case):
+    B, N, H, W, C = (case[k] for k in ("B", "N", "H", "W", "C"))
+    params, G = workloads.make_custom(B, N, H, W, C, seed=B * 7 + N)
+    check(orc, params, G, H, W, fmt)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_reduced_precision_benchmark_shape(orc, fmt):
+    wl, params, G = workloads.make_inputs(2)
+    check(orc, params, G, wl.H, wl.W, fmt, frames=[0, 151, 383])
+
+
+def test_reduced_precision_rejects_unknown_format():
+    from differentiable_gaussian_splatting_pdr_amd import _lib
+    L = _lib.lib()
+    assert L.pdr_splat_forward_fmt(0x10000, 0x10000, 3, 1, 4, 8, 8, 1, 3.0, 0x10000, 1 << 20, None) == -1
+    assert L.pdr_splat_backward_fmt(0x10000, 0x10000, -1, 0x10000, 1, 4, 8, 8, 1, 3.0, 0x10000,
+                                    1 << 20, 0, None) == -1
