@@ -40,6 +40,7 @@ EXPORTED = (
     "pdr_params_activate_backward",
     "pdr_splat_forward_fmt",
     "pdr_splat_backward_fmt",
+    "pdr_splat_backward_algo",
 )
 
 KERNEL_COUNT = 14
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.pdr_splat_forward_fmt.restype = i
         L.pdr_splat_backward_fmt.argtypes = [vp, vp, i, vp, i, i, i, i, i, f, vp, sz, i, vp]
         L.pdr_splat_backward_fmt.restype = i
+        L.pdr_splat_backward_algo.argtypes = [vp, vp, i, vp, i, i, i, i, i, f, vp, sz, i, i, vp]
+        L.pdr_splat_backward_algo.restype = i
         _lib = L
     return _lib
 
@@ -225,3 +228,14 @@ def pdr_splat_backward_fmt(params, grad_image, grad_format, grad_params, B, N, H
                                                B, N, H, W, C, float(radius), workspace,
                                                workspace_bytes, int(reuse_binning), stream),
                   "pdr_splat_backward_fmt")
+
+
+PDR_BWD_AUTO, PDR_BWD_TILE, PDR_BWD_SPAN = 0, 1, 2
+
+
+def pdr_splat_backward_algo(params, grad_image, grad_format, grad_params, B, N, H, W, C, radius,
+                            workspace, workspace_bytes, reuse_binning, algo, stream):
+    return _raise(lib().pdr_splat_backward_algo(params, grad_image, int(grad_format), grad_params,
+                                                B, N, H, W, C, float(radius), workspace,
+                                                workspace_bytes, int(reuse_binning), int(algo),
+                                                stream), "pdr_splat_backward_algo")

@@ -12,7 +12,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = ["csrc/bin.hip", "csrc/raster.hip", "csrc/loss.hip", "csrc/adapter.hip", "csrc/abi.hip",
+SOURCES = ["csrc/bin.hip", "csrc/raster.hip", "csrc/loss.hip", "csrc/adapter.hip", "csrc/span.hip",
+           "csrc/abi.hip",
            "csrc/timing.hip"]
 LIB = os.path.join(PKG, "libpdrsplat.so")
 

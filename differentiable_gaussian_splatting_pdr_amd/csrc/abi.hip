@@ -53,6 +53,12 @@ int layout_for(const Dims &d, void *ws, size_t bytes, Layout *L) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PDR_OK : PDR_ERR_HIP; }
 
+// Which backward PDR_BWD_AUTO takes where both apply.
+#ifndef PDR_AUTO_SPAN
+#define PDR_AUTO_SPAN 0
+#endif
+constexpr bool kAutoSpan = PDR_AUTO_SPAN != 0;
+
 // Forward (binning + raster) into image with Cp leading pixel-branch
 // channels per pixel (Cp = 0: the plain layout).
 int forward_impl(const float *params, const float *pixel, int Cp, void *image, int B, int N,
@@ -80,7 +86,7 @@ int forward_impl(const float *params, const float *pixel, int Cp, void *image, i
 int backward_impl(const float *params, const void *grad_image, int Cp, float *grad_params,
                   float *grad_pixel, int B, int N, int H, int W, int C, float radius,
                   void *workspace, size_t workspace_bytes, int reuse_binning, void *stream,
-                  int fmt = PDR_FMT_F32) {
+                  int fmt = PDR_FMT_F32, int algo = PDR_BWD_AUTO) {
   Dims d;
   Layout L;
   if (!params || !grad_image || !grad_params) return PDR_ERR_INVALID_ARG;
@@ -90,9 +96,20 @@ int backward_impl(const float *params, const void *grad_image, int Cp, float *gr
   if (rc == PDR_OK && (long long)B * H * W * (Cp + (long long)C) > (1LL << 46)) rc = PDR_ERR_INVALID_ARG;
   if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
   if (rc != PDR_OK) return rc;
+  if (algo != PDR_BWD_AUTO && algo != PDR_BWD_TILE && algo != PDR_BWD_SPAN) return PDR_ERR_INVALID_ARG;
+  const bool span_ok = Cp == 0 && span_backward_supported(H, W, C);
+  if (algo == PDR_BWD_SPAN && !span_ok) return PDR_ERR_INVALID_ARG;
+  const bool span = algo == PDR_BWD_SPAN || (algo == PDR_BWD_AUTO && span_ok && kAutoSpan);
   hipStream_t st = (hipStream_t)stream;
   char *w = (char *)workspace;
   hipError_t e = hipSuccess;
+  if (span) {
+    if (!reuse_binning) e = launch_preprocess(params, B, N, H, W, C, radius, workspace, L, true, st);
+    if (e == hipSuccess)
+      e = launch_backward_span(params, grad_image, grad_params, B, N, H, W, C, radius, workspace, L,
+                               reuse_binning != 0, st, fmt);
+    return hip_status(e);
+  }
   if (!reuse_binning)
     e = launch_binning(params, B, N, H, W, C, radius, workspace, L, (int *)(w + L.tile_off),
                        (int *)(w + L.list), L.cap, true, st);
@@ -152,6 +169,14 @@ int pdr_splat_backward_fmt(const float *params, const void *grad_image, int grad
                            void *stream) {
   return backward_impl(params, grad_image, 0, grad_params, nullptr, B, N, H, W, C, radius,
                        workspace, workspace_bytes, reuse_binning, stream, grad_format);
+}
+
+int pdr_splat_backward_algo(const float *params, const void *grad_image, int grad_format,
+                            float *grad_params, int B, int N, int H, int W, int C, float radius,
+                            void *workspace, size_t workspace_bytes, int reuse_binning, int algo,
+                            void *stream) {
+  return backward_impl(params, grad_image, 0, grad_params, nullptr, B, N, H, W, C, radius,
+                       workspace, workspace_bytes, reuse_binning, stream, grad_format, algo);
 }
 
 int pdr_splat_forward_concat(const float *params, const float *pixel, int Cp, float *out, int B,

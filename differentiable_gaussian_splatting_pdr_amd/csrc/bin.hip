@@ -256,6 +256,18 @@ static void choose_groups(int B, int N, int nTx, int nTy, int *gh, int *NC) {
   *gh = rows < 1 ? 1 : (int)rows;
 }
 
+hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, int C, float radius,
+                             void *ws, const Layout &L, bool stamp_valid, hipStream_t st) {
+  char *w = (char *)ws;
+  long long BN = (long long)B * N;
+  PDR_TIMED(PDR_K_PREPROCESS, st,
+            hipLaunchKernelGGL(k_preprocess, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,
+                               params, (int)BN, C, H, W, radius, (GRec *)(w + L.recs),
+                               (uint2 *)(w + L.boxes), (WsHeader *)(w + L.hdr), N,
+                               stamp_valid ? (unsigned long long)(uintptr_t)params : 0ull));
+  return hipGetLastError();
+}
+
 hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C, float radius,
                           void *ws, const Layout &L, int *tile_off, int *list, long long cap,
                           bool stamp_valid, hipStream_t st) {
@@ -267,10 +279,7 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   int *gtot = (int *)(w + L.gtot);
   long long BN = (long long)B * N;
   int nTx = (W + kTileW - 1) / kTileW, nTy = (H + kTileH - 1) / kTileH;
-  PDR_TIMED(PDR_K_PREPROCESS, st,
-            hipLaunchKernelGGL(k_preprocess, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,
-                               params, (int)BN, C, H, W, radius, recs, boxes, hdr, N,
-                               stamp_valid ? (unsigned long long)(uintptr_t)params : 0ull));
+  launch_preprocess(params, B, N, H, W, C, radius, ws, L, stamp_valid, st);
   int gh, NC;
   choose_groups(B, N, nTx, nTy, &gh, &NC);
   int G = (nTy + gh - 1) / gh;

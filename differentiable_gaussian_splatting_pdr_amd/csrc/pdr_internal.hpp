@@ -29,6 +29,17 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
                           void *ws, const Layout &L, int *tile_off, int *list, long long cap,
                           bool stamp_valid, hipStream_t st);
 
+// Per-Gaussian records only (the first step of launch_binning).
+hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, int C, float radius,
+                             void *ws, const Layout &L, bool stamp_valid, hipStream_t st);
+
+// Tile-free backward (one wave per Gaussian over its support spans, fused
+// chain rule); needs only the records.  C <= 16, H*W*C < 2^29, plain layout.
+bool span_backward_supported(int H, int W, int C);
+hipError_t launch_backward_span(const float *params, const void *grad_image, float *grad_params,
+                                int B, int N, int H, int W, int C, float radius, void *ws,
+                                const Layout &L, bool check_stamp, hipStream_t st, int fmt);
+
 // Forward raster: image[b][y][x][c] for all channels.  With Cp > 0 the
 // output has Cp + C channels per pixel: pixel[b][y][x][0..Cp) first, then the
 // rendered channels (concat fusion).

@@ -99,8 +99,9 @@ def forward(params: torch.Tensor, H: int, W: int, radius: float = 3.0,
 def backward(params: torch.Tensor, grad_image: torch.Tensor, H: int, W: int,
              radius: float = 3.0, workspace: Workspace | None = None,
              reuse_binning: bool = False, grad_params: torch.Tensor | None = None,
-             check: bool = True):
-    """dL/dparams for dL/dimage; returns grad_params."""
+             check: bool = True, algo: int | None = None):
+    """dL/dparams for dL/dimage; returns grad_params.  algo: None (the
+    library default) or _lib.PDR_BWD_TILE / PDR_BWD_SPAN."""
     B, N, C = _check_params(params)
     dev = params.device
     if grad_image.shape != (B, H, W, C) or grad_image.dtype not in _FMT:
@@ -113,7 +114,12 @@ def backward(params: torch.Tensor, grad_image: torch.Tensor, H: int, W: int,
         reuse_binning = False
         workspace = Workspace(dev, Workspace.bytes_for(B, N, H, W, C, _initial_pairs(B, N, H, W)))
     for _ in range(2):
-        if grad_image.dtype == torch.float32:
+        if algo is not None:
+            _lib.pdr_splat_backward_algo(params.data_ptr(), grad_image.data_ptr(),
+                                         _FMT[grad_image.dtype], grad_params.data_ptr(), B, N, H,
+                                         W, C, radius, workspace.ptr, workspace.nbytes,
+                                         int(reuse_binning), algo, st)
+        elif grad_image.dtype == torch.float32:
             _lib.pdr_splat_backward(params.data_ptr(), grad_image.data_ptr(),
                                     grad_params.data_ptr(), B, N, H, W, C, radius, workspace.ptr,
                                     workspace.nbytes, int(reuse_binning), st)

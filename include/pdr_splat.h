@@ -167,6 +167,27 @@ int pdr_splat_backward_fmt(const float *params, const void *grad_image, int grad
                            void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Backward algorithms.  PDR_BWD_TILE: the tile raster (16x16 tiles, one
+ * wave each, per-(tile, Gaussian) wave reduction and one atomic per sum,
+ * then a finalisation pass).  PDR_BWD_SPAN: tile-free (page 3 of the
+ * sources, first paragraph, pairs tile-free splat processing with subgroup
+ * gradient reduction): one wave per Gaussian walks the pixel spans of its
+ * truncated ellipse row by row, packed 64 pixels at a time, reduces once
+ * per Gaussian and stores the finished gradient row (no atomics, no
+ * zeroing, no finalisation pass); it needs only the per-Gaussian records, so
+ * without reuse it runs no tile binning.  C <= 16 and H*W*C < 2^29.  PDR_BWD_AUTO: the
+ * library's default (what pdr_splat_backward uses).  Both compute the same
+ * sums within the same tolerance. */
+typedef enum { PDR_BWD_AUTO = 0, PDR_BWD_TILE = 1, PDR_BWD_SPAN = 2 } pdr_backward_algo;
+
+/* pdr_splat_backward_fmt with an explicit algorithm; PDR_ERR_INVALID_ARG for
+ * PDR_BWD_SPAN outside its limits or an unknown algorithm. */
+int pdr_splat_backward_algo(const float *params, const void *grad_image, int grad_format,
+                            float *grad_params, int B, int N, int H, int W, int C, float radius,
+                            void *workspace, size_t workspace_bytes, int reuse_binning, int algo,
+                            void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Concat fusion ("Learning Video Dynamics with Predictive Differentiable
  * Rendering", reading notes, "Core Idea" and "Relation To Prior Work": the
  * Gaussian branch's rendered frame is fused with the pixel branch's coarse

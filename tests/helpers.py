@@ -21,8 +21,9 @@ ATOL = 1e-5
 RTOL = 1e-4
 
 
-def gpu_forward_backward(params, grad_image, H, W, radius=3.0, reuse=True):
-    """Run forward then backward through the library; numpy in, numpy out."""
+def gpu_forward_backward(params, grad_image, H, W, radius=3.0, reuse=True, algo=None):
+    """Run forward then backward through the library; numpy in, numpy out.
+    algo: None (library default) or a PDR_BWD_* backward algorithm."""
     import torch
     from differentiable_gaussian_splatting_pdr_amd import splat
 
@@ -32,7 +33,7 @@ def gpu_forward_backward(params, grad_image, H, W, radius=3.0, reuse=True):
     out = {"image": image.cpu().numpy()}
     if grad_image is not None:
         g = torch.from_numpy(np.ascontiguousarray(grad_image, dtype=np.float32)).to(dev)
-        gp = splat.backward(p, g, H, W, radius, workspace=ws, reuse_binning=reuse)
+        gp = splat.backward(p, g, H, W, radius, workspace=ws, reuse_binning=reuse, algo=algo)
         out["grad"] = gp.cpu().numpy()
     torch.cuda.synchronize()
     return out
