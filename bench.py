@@ -126,6 +126,32 @@ def adapter_leg(args, _lib, torch, B, N, H, W, C, params, image, grad_image, tar
     return res
 
 
+def backward_algo_leg(args, _lib, torch, B, N, H, W, C, params, grad_image, grad_params, ws,
+                      ws_bytes, st):
+    """The backward alone (reusing the forward's binning) with each algorithm:
+    the tile raster and the tile-free span walk (C <= 16)."""
+    out = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, algo in (("tile", _lib.PDR_BWD_TILE), ("span", _lib.PDR_BWD_SPAN)):
+        if algo == _lib.PDR_BWD_SPAN and C > 16:
+            continue
+
+        def run():
+            _lib.pdr_splat_backward_algo(params.data_ptr(), grad_image.data_ptr(), 0,
+                                         grad_params.data_ptr(), B, N, H, W, C, args.radius,
+                                         ws.data_ptr(), ws_bytes, 1, algo, st)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_backward_ms"] = round(e0.elapsed_time(e1) / args.steps, 5)
+    return out
+
+
 def source_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -333,6 +359,8 @@ def main():
 
     adapter_out = adapter_leg(args, _lib, torch, B, N, H, W, C, params, image, grad_image, target,
                               ws, ws_bytes, st, step)
+    algo_out = backward_algo_leg(args, _lib, torch, B, N, H, W, C, params, grad_image, grad_params,
+                                 ws, ws_bytes, st)
 
     cpu, support_pairs = None, None
     if not args.no_cpu_baseline:
@@ -397,6 +425,7 @@ def main():
         "cpu_baseline": cpu,
         "loss": loss_out,
         "adapter": adapter_out,
+        "backward_algorithms": algo_out,
     }
     print(json.dumps(out), flush=True)
 

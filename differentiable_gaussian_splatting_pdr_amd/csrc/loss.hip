@@ -42,7 +42,11 @@ namespace {
 
 constexpr int kTaps = 11;               // window taps per axis
 constexpr int kHalf = 5;                // window radius
-constexpr int kLossRows = 2;            // rows staged per LDS buffer
+#ifndef PDR_LOSS_ROWS
+#define PDR_LOSS_ROWS 2
+#endif
+constexpr int kLossRows = PDR_LOSS_ROWS;  // rows staged per LDS buffer (2 or 4)
+static_assert(kLossRows == 2 || kLossRows == 4, "rows per chunk");
 constexpr int kLossMaxThreads = 512;    // threads of a workgroup (flat columns)
 constexpr int kLossMaxCg = 16;          // channels of one group
 constexpr int kLossMaxL = kLossMaxThreads + 2 * kHalf * kLossMaxCg;  // staged run length
@@ -331,16 +335,21 @@ PDR_LOSS_KERNEL void k_ssim_fwd(
     const uint32_t so = emit ? (uint32_t)(yin - kHalf) * w.rowb : 0u;
     fwd_step<CG, decltype(Jc)::value>(h, rq, g.cg, tp, emit, c1, c2, w.ocol, so, out);
   };
-  // one staged chunk (kLossRows = 2 rows); the 11 chunks of an outer
-  // iteration cover 22 rows, so every ring phase is a compile-time constant
+  // one staged chunk of kLossRows rows; the 11 chunks of an outer
+  // iteration cover 11 kLossRows rows, so every ring phase is a compile-time
+  // constant
   auto chunk = [&](auto Cc, int ch0) {
     constexpr int c = decltype(Cc)::value;
     const int ch = ch0 + c;
     if (ch >= w.nch) return;
     const int buf = ch & 1;
     if (ch + 1 < w.nch) load_chunk(pre_x, pre_y, ch + 1);
-    row(IC<(2 * c) % kTaps>{}, 2 * ch, buf, 0);
-    row(IC<(2 * c + 1) % kTaps>{}, 2 * ch + 1, buf, 1);
+    row(IC<(kLossRows * c) % kTaps>{}, kLossRows * ch, buf, 0);
+    row(IC<(kLossRows * c + 1) % kTaps>{}, kLossRows * ch + 1, buf, 1);
+    if constexpr (kLossRows == 4) {
+      row(IC<(kLossRows * c + 2) % kTaps>{}, kLossRows * ch + 2, buf, 2);
+      row(IC<(kLossRows * c + 3) % kTaps>{}, kLossRows * ch + 3, buf, 3);
+    }
     if (ch + 1 < w.nch) store_chunk(buf ^ 1);
     __syncthreads();
   };
@@ -490,8 +499,12 @@ PDR_LOSS_KERNEL void k_ssim_bwd(
       yo[r] = ld(ry, vo, so);
     }
     if (ch + 1 < w.nch) load_chunk(pre, ch + 1);
-    row(IC<(2 * c) % kTaps>{}, 2 * ch, buf, 0, xo[0], yo[0]);
-    row(IC<(2 * c + 1) % kTaps>{}, 2 * ch + 1, buf, 1, xo[1], yo[1]);
+    row(IC<(kLossRows * c) % kTaps>{}, kLossRows * ch, buf, 0, xo[0], yo[0]);
+    row(IC<(kLossRows * c + 1) % kTaps>{}, kLossRows * ch + 1, buf, 1, xo[1], yo[1]);
+    if constexpr (kLossRows == 4) {
+      row(IC<(kLossRows * c + 2) % kTaps>{}, kLossRows * ch + 2, buf, 2, xo[2], yo[2]);
+      row(IC<(kLossRows * c + 3) % kTaps>{}, kLossRows * ch + 3, buf, 3, xo[3], yo[3]);
+    }
     if (ch + 1 < w.nch) store_chunk(buf ^ 1);
     __syncthreads();
   };

@@ -304,61 +304,6 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
     if (vidx < CP) slot = vidx < cc ? 5 + c0 + vidx : -1;
     else if (vidx < K) slot = vidx - CP;
   }
-  // Two entries' sums fit one 16-value reduction when 2 K <= 16 (C <= 3):
-  // entries with work are then reduced in pairs, which costs far less than
-  // two 8-value reductions (the first butterfly stages dominate).
-  constexpr bool kPair = 2 * K <= 16 && KP == 8;
-  int slot2 = -1;
-  bool second = false;
-  if (kPair && lane < 16) {
-    const int v2 = value_index<16>(lane);
-    second = v2 >= 8;
-    const int v = v2 & 7;
-    if (v < CP) slot2 = v < cc ? 5 + c0 + v : -1;
-    else if (v < K) slot2 = v - CP;
-  }
-
-  // One entry's per-lane partial sums into part[0 .. K); false if no pixel
-  // of the wave is inside its support.
-  auto eval = [&](const Entry<CP> &r, unsigned int um, float *part) -> bool {
-    float a[CP];
-#pragma unroll
-    for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < UY; ++j) {
-      if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
-      const float dy = (fy + (float)(UH * j)) - r.my;
-#pragma unroll
-      for (int i = 0; i < UX; ++i) {
-        if (!(um & (1u << (j * UX + i)))) continue;
-        const float dx = (fx + (float)(UW * i)) - r.mx;
-        const float u1 = r.l11 * dx + r.l12 * dy;
-        const float u2 = r.l21 * dx + r.l22 * dy;
-        const float q = u1 * u1 + u2 * u2;
-        const bool inside = q <= thr;
-        if (__builtin_amdgcn_ballot_w64(inside) == 0ull) continue;
-        any = true;
-        const float w = inside ? __builtin_amdgcn_exp2f(-q) : 0.f;
-        float h = 0.f;
-#pragma unroll
-        for (int c = 0; c < CP; ++c) h += G[j][i][c] * a[c];
-        const float v = h * w;
-#pragma unroll
-        for (int c = 0; c < CP; ++c) part[c] += G[j][i][c] * w;
-        const float t1 = v * u1, t2 = v * u2;
-        part[CP + 0] += t1;
-        part[CP + 1] += t2;
-        part[CP + 2] += t1 * u1;
-        part[CP + 3] += t2 * u2;
-        part[CP + 4] += t1 * u2;
-      }
-    }
-    return any;
-  };
-  auto unit_mask = [&](int e) -> unsigned int {
-    return (__builtin_amdgcn_readfirstlane(s[e].mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
-  };
 
   const int beg = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t]);
   const int end = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t + 1]);
@@ -368,32 +313,47 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
     stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0);
     __syncthreads();
     for (int e = 0; e < cnt; ++e) {
-      const unsigned int um = unit_mask(e);
+      const unsigned int um =
+          (__builtin_amdgcn_readfirstlane(s[e].mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
       if (um == 0u) continue;
-      if constexpr (kPair) {
-        int e2 = e + 1;
-        unsigned int um2 = 0u;
-        while (e2 < cnt && (um2 = unit_mask(e2)) == 0u) ++e2;
-        if (e2 < cnt) {
-          const Entry<CP> ra = s[e], rb = s[e2];
-          float part[16];
-#pragma unroll
-          for (int k = 0; k < 16; ++k) part[k] = 0.f;
-          const bool anya = eval(ra, um, part);
-          const bool anyb = eval(rb, um2, part + 8);
-          e = e2;
-          if (!anya && !anyb) continue;
-          const float tot = wave_reduce_transposed<16>(part, lane);
-          if (slot2 >= 0 && (second ? anyb : anya))
-            unsafeAtomicAdd(sums + (unsigned)((second ? rb.row : ra.row) + slot2), tot);
-          continue;
-        }
-      }
       const Entry<CP> r = s[e];
+      float a[CP];
+#pragma unroll
+      for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
       float part[KP];
 #pragma unroll
       for (int k = 0; k < KP; ++k) part[k] = 0.f;
-      if (!eval(r, um, part)) continue;
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < UY; ++j) {
+        if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
+        const float dy = (fy + (float)(UH * j)) - r.my;
+#pragma unroll
+        for (int i = 0; i < UX; ++i) {
+          if (!(um & (1u << (j * UX + i)))) continue;
+          const float dx = (fx + (float)(UW * i)) - r.mx;
+          const float u1 = r.l11 * dx + r.l12 * dy;
+          const float u2 = r.l21 * dx + r.l22 * dy;
+          const float q = u1 * u1 + u2 * u2;
+          const bool inside = q <= thr;
+          if (__builtin_amdgcn_ballot_w64(inside) == 0ull) continue;
+          any = true;
+          const float w = inside ? __builtin_amdgcn_exp2f(-q) : 0.f;
+          float h = 0.f;
+#pragma unroll
+          for (int c = 0; c < CP; ++c) h += G[j][i][c] * a[c];
+          const float v = h * w;
+#pragma unroll
+          for (int c = 0; c < CP; ++c) part[c] += G[j][i][c] * w;
+          const float t1 = v * u1, t2 = v * u2;
+          part[CP + 0] += t1;
+          part[CP + 1] += t2;
+          part[CP + 2] += t1 * u1;
+          part[CP + 3] += t2 * u2;
+          part[CP + 4] += t1 * u2;
+        }
+      }
+      if (!any) continue;
       const float tot = wave_reduce_transposed<KP>(part, lane);
       if (slot >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot), tot);
     }
