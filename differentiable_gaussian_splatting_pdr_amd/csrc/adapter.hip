@@ -29,27 +29,6 @@ namespace pdr {
 
 namespace {
 
-// q = n / d for 0 <= n < 2^31 by multiply and shift (round-up method of
-// Granlund and Montgomery, "Division by invariant integers using
-// multiplication"): l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
-// q = (umulhi(n, m) + n) >> l.
-struct FastDiv {
-  uint32_t d, m, l;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-  FastDiv f;
-  f.d = d;
-  f.l = 0;
-  while ((1ull << f.l) < d) ++f.l;
-  f.m = (uint32_t)((((1ull << f.l) - d) << 32) / d + 1);
-  return f;
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
-  return (__umulhi(n, f.m) + n) >> f.l;
-}
-
 struct GridArgs {
   FastDiv row;   // 5 + C values per Gaussian
   FastDiv nper;  // N Gaussians per frame

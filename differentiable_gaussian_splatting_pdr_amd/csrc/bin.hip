@@ -45,12 +45,20 @@ __device__ __forceinline__ float clamp_to_float(double v) {
   return (float)fmin(fmax(v, -m), m);
 }
 
+// One workgroup per 256 Gaussians: their parameter rows (5 + C floats each)
+// are read with coalesced loads, the first five values of every row staged
+// in LDS and any non-finite value flagged, then each thread builds one
+// Gaussian's record.
 __global__ __launch_bounds__(256) void k_preprocess(const float *__restrict__ params, int BN, int C,
-                                                    int H, int W, float radius,
+                                                    FastDiv pdiv, int H, int W, float radius,
                                                     GRec *__restrict__ recs,
                                                     uint2 *__restrict__ boxes, WsHeader *hdr,
                                                     int stamp_N, unsigned long long stamp_ptr) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ float s5[5][256];
+  __shared__ int bad[256];
+  const int tid = threadIdx.x;
+  const int g0 = blockIdx.x * 256;
+  const int i = g0 + tid;
   if (i == 0) {
     hdr->stamp[0] = BN / stamp_N;
     hdr->stamp[1] = stamp_N;
@@ -61,12 +69,23 @@ __global__ __launch_bounds__(256) void k_preprocess(const float *__restrict__ pa
     hdr->stamp[6] = (int)(unsigned)(stamp_ptr & 0xffffffffull);
     hdr->stamp[7] = (int)(unsigned)(stamp_ptr >> 32);
   }
-  if (i >= BN) return;
-  const float *g = params + (size_t)i * (5 + C);
-  float mx = g[0], my = g[1], s1 = g[2], s2 = g[3], th = g[4];
-  bool ok = isfinite(mx) && isfinite(my) && isfinite(s1) && isfinite(s2) && isfinite(th) &&
-            s1 > 0.f && s2 > 0.f;
-  for (int c = 0; c < C; ++c) ok = ok && isfinite(g[5 + c]);
+  bad[tid] = 0;
+  __syncthreads();
+  const int ng = min(256, BN - g0);
+  const uint32_t P = pdiv.d;
+  const uint32_t tot = (uint32_t)ng * P;
+  const float *src = params + (size_t)g0 * P;
+  for (uint32_t e = tid; e < tot; e += 256) {
+    const float v = src[e];
+    const uint32_t g = fdiv(e, pdiv);
+    const uint32_t k = e - g * P;
+    if (k < 5) s5[k][g] = v;
+    if (!isfinite(v)) bad[g] = 1;
+  }
+  __syncthreads();
+  if (tid >= ng) return;
+  float mx = s5[0][tid], my = s5[1][tid], s1 = s5[2][tid], s2 = s5[3][tid], th = s5[4][tid];
+  const bool ok = !bad[tid] && s1 > 0.f && s2 > 0.f;
   GRec r;
   r.mx = mx;
   r.my = my;
@@ -177,12 +196,29 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
   }
 
   const uint2 *fb = boxes + (size_t)b * N;
+  // the boxes of a chunk are loaded all at once, one chunk ahead, so the
+  // loads of the next chunk are in flight while this one is binned
+  constexpr int kPer = kMaxChunk / kBinThreads;
+  uint2 nxt[kPer];
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kBinThreads;
+      nxt[k] = (i < NC && c + i < N) ? fb[c + i] : make_uint2(kEmptyBox, kEmptyBox);
+    }
+  };
+  load_chunk(0);
   for (int c0 = 0; c0 < N; c0 += NC) {
+    uint2 cur[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) cur[k] = nxt[k];
     for (int w = tid; w < Tg * words; w += kBinThreads) bits[w] = 0u;
     __syncthreads();
-    const int cn = min(NC, N - c0);
-    for (int i = tid; i < cn; i += kBinThreads) {
-      uint2 bx = fb[c0 + i];
+    if (c0 + NC < N) load_chunk(c0 + NC);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kBinThreads;
+      const uint2 bx = cur[k];
       int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
       int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
       if (x0 > x1) continue;
@@ -262,7 +298,8 @@ hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, in
   long long BN = (long long)B * N;
   PDR_TIMED(PDR_K_PREPROCESS, st,
             hipLaunchKernelGGL(k_preprocess, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,
-                               params, (int)BN, C, H, W, radius, (GRec *)(w + L.recs),
+                               params, (int)BN, C, make_fastdiv((uint32_t)(5 + C)), H, W, radius,
+                               (GRec *)(w + L.recs),
                                (uint2 *)(w + L.boxes), (WsHeader *)(w + L.hdr), N,
                                stamp_valid ? (unsigned long long)(uintptr_t)params : 0ull));
   return hipGetLastError();

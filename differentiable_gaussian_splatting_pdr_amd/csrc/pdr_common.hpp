@@ -60,6 +60,27 @@ struct Layout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// q = n / d for 0 <= n < 2^31 by multiply and shift (round-up method of
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication"): l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+// q = (umulhi(n, m) + n) >> l.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  f.l = 0;
+  while ((1ull << f.l) < d) ++f.l;
+  f.m = (uint32_t)((((1ull << f.l) - d) << 32) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+  return (__umulhi(n, f.m) + n) >> f.l;
+}
+
 // BR: tile rows of the batch (B * ceil(H / tile)), an upper bound on the
 // binning's row bands.
 inline Layout make_layout(long long BN, long long BT, long long BR, long long cap) {

@@ -19,7 +19,10 @@ void timing_end(int kid, hipStream_t st);
 
 constexpr int kMaxGroupTiles = 1024;    // tiles of one binning group (static LDS bases)
 constexpr long long kMaxChunk = 4096;   // Gaussians per binning chunk (bit-matrix columns)
-constexpr long long kBinTargetGroups = 2048;  // binning workgroups to aim for
+#ifndef PDR_BIN_TARGET_GROUPS
+#define PDR_BIN_TARGET_GROUPS 2048
+#endif
+constexpr long long kBinTargetGroups = PDR_BIN_TARGET_GROUPS;  // binning workgroups to aim for
 constexpr long long kBinLdsBytes = 60 * 1024;  // + 4 KB of static bases stays within 64 KB
 
 // K1 + count + scan + list write; tile_off/list may be the workspace's own

@@ -364,27 +364,24 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
 // apply the chain rule in place (fp64):
 //   dmu = L^T (S1, S2) with L = [[c/s1, s/s1], [-s/s2, c/s2]],
 //   ds1 = S11/s1, ds2 = S22/s2, dtheta = (s1/s2 - s2/s1) S12, da = A
-// undoing the kappa scale of the whitened coordinates.
+// undoing the kappa scale of the whitened coordinates.  A Gaussian whose
+// record has an empty box (culled, or with no pixel in the frame) is in no
+// tile list: its row was zeroed and stays zero, so only its record is read.
 __global__ __launch_bounds__(256) void k_finalize(const float *__restrict__ params,
+                                                  const GRec *__restrict__ recs,
                                                   float *__restrict__ grad, long long BN, int C,
                                                   const WsHeader *hdr) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= BN) return;
   if (hdr->status & (kStatusOverflow | kStatusStale)) return;
+  const GRec r = recs[i];
+  if ((r.bx & 0xFFFFu) > (r.bx >> 16) || (r.by & 0xFFFFu) > (r.by >> 16)) return;
   const int P = 5 + C;
   const float *g = params + i * P;
   float *o = grad + i * P;
-  float mx = g[0], my = g[1], s1f = g[2], s2f = g[3], th = g[4];
-  bool ok = isfinite(mx) && isfinite(my) && isfinite(s1f) && isfinite(s2f) && isfinite(th) &&
-            s1f > 0.f && s2f > 0.f;
-  for (int c = 0; c < C; ++c) ok = ok && isfinite(g[5 + c]);
-  if (!ok) {
-    for (int c = 0; c < P; ++c) o[c] = 0.f;
-    return;
-  }
   double sn, cs;
-  sincos((double)th, &sn, &cs);
-  const double s1 = s1f, s2 = s2f;
+  sincos((double)g[4], &sn, &cs);
+  const double s1 = g[2], s2 = g[3];
   const double S1 = o[0], S2 = o[1], S11 = o[2], S22 = o[3], S12 = o[4];
   o[0] = (float)(((cs / s1) * S1 - (sn / s2) * S2) / kKappa);
   o[1] = (float)(((sn / s1) * S1 + (cs / s2) * S2) / kKappa);
@@ -548,7 +545,8 @@ hipError_t launch_backward(const float *params, const void *grad_image, float *g
   }
   PDR_TIMED(PDR_K_FINALIZE, st,
             hipLaunchKernelGGL(k_finalize, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,
-                               params, grad_params, BN, C, (const WsHeader *)hdr));
+                               params, (const GRec *)((char *)ws + L.recs), grad_params, BN, C,
+                               (const WsHeader *)hdr));
   return hipGetLastError();
 }
 
