@@ -65,6 +65,7 @@ def test_workspace_bytes_layout():
     (0, 10, 16, 16, 1, 0), (1, 0, 16, 16, 1, 0), (1, 10, 0, 16, 1, 0), (1, 10, 16, 0, 1, 0),
     (1, 10, 16, 16, 0, 0), (1, 10, 16, 16, 1, -1), (1, 10, 40000, 16, 1, 0),
     (1, 10, 16, 16, 1, 2 ** 31), (1 << 20, 1 << 12, 16, 16, 1, 0), (1 << 14, 1 << 14, 16, 16, 3, 0),
+    (1, (1 << 22) + 1, 16, 16, 1, 0), (1, 10, 16, 16385, 1, 0), (1, 10, 32768, 16, 1, 0),
 ])
 def test_workspace_bytes_rejects(args):
     with pytest.raises(_lib.PdrError) as e:
