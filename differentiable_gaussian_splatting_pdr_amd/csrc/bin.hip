@@ -2,14 +2,15 @@
 //
 //  k_preprocess   one thread per Gaussian: validity, fp64 pixel bounding box
 //                 of the truncated ellipse q <= k^2, whitening rows.
-//  k_bin<false>   per (frame, tile group): per-tile overlap counts.
-//  k_bin<true>    per (frame, tile group): the per-tile lists, ascending
+//  k_bin<false,M> per (frame, tile group): per-tile overlap counts.
+//  k_bin<true,M>  per (frame, tile group): the per-tile lists, ascending
 //                 Gaussian index, at the scanned offsets.
 //
-// A tile group holds a rectangle of tiles and walks the frame's Gaussians in
-// chunks; for each chunk it builds an LDS bit matrix [tile][Gaussian] of box
-// overlaps and compacts every tile's bit row with a wave scan.  The lists are
-// thus produced in ascending order with no sort and no global atomics.
+// A tile group holds a band of tile rows and walks the frame's Gaussians in
+// chunks (consecutive Gaussians, or, M = true, the band's members); for each
+// chunk it builds an LDS bit matrix [tile][Gaussian] of box overlaps and
+// compacts every tile's bit row with a wave scan.  The lists are thus
+// produced in ascending order with no sort and no global atomics.
 #include "pdr_common.hpp"
 #include "pdr_internal.hpp"
 
@@ -124,16 +125,33 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
 }
 
 // LDS bit matrix binning.  Grid: G bands x B frames (1D, XCD-aware); a group is
-// a band of gh whole tile rows.  Dynamic LDS: Tg * (NC / 32) words, NC a
-// multiple of 64.
+// a band of gh whole tile rows.  Dynamic LDS: Tg * (NC / 32) words of bits
+// (NC a multiple of 64), then, with MEMBERS, NC member indices.
+//
+// A chunk is a set of at most NC Gaussians in ascending index order; each
+// sets, in its column, the bits of the band's tiles its box overlaps, each
+// tile's bit row is compacted with a wave scan and the columns map back to
+// Gaussian indices.  Lists thus come out ascending with no sort and no
+// global atomics.  Two ways of forming chunks:
+//  MEMBERS = false  chunk = NC consecutive Gaussians of the frame, loaded one
+//                   chunk ahead; every tile row compacts all NC columns.
+//  MEMBERS = true   the group scans the frame's boxes in segments (loaded one
+//                   segment ahead) and gathers the band's members -- the
+//                   Gaussians whose box meets the band -- into an LDS list in
+//                   index order (wave ballots, a prefix over waves); NC
+//                   members form a chunk.  A band then pays for bit setting
+//                   and compaction on its own members only, which wins when
+//                   a frame has many bands.
 //
 // Count pass (WRITE = false): per-tile counts and the group's total.
 // Write pass (WRITE = true): the group's base offset is the sum of the
 // totals of all groups before it (frame-major, bands top to bottom); an
 // exclusive scan (wave64 DPP scan) of its tiles' counts gives their
 // offsets; then the lists are written.  The last group writes the pair
-// total and the overflow flag.
-template <bool WRITE>
+// total and the overflow flag.  Both passes form the same chunks.
+constexpr int kSegSlots = 4;   // boxes per thread per member-scan segment
+
+template <bool WRITE, bool MEMBERS>
 __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ boxes, int B, int N,
                                                      int nTx, int nTy, int gh, int G, int NC,
                                                      int *__restrict__ counts,
@@ -141,10 +159,11 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
                                                      int *__restrict__ tile_off,
                                                      int *__restrict__ list, long long cap,
                                                      WsHeader *hdr) {
-  extern __shared__ unsigned int bits[];
+  extern __shared__ unsigned int dyn[];
   __shared__ int base[kMaxGroupTiles];
   __shared__ long long red[kBinThreads / kWave];
   __shared__ int wtot[kBinThreads / kWave];
+  __shared__ int wcnt[kSegSlots][kBinThreads / kWave];
   int b, g;  // frame, band: all bands of a frame on one XCD, so its boxes stay in that L2
   if (!xcd_frame_item(blockIdx.x, G, B, &b, &g)) return;
   const int ty0 = g * gh;
@@ -154,6 +173,8 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
   const size_t t0 = (size_t)b * nT + (size_t)ty0 * nTx;  // first tile of the group
   const int words = NC >> 5;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned int *bits = dyn;
+  int *mem = (int *)(dyn + (size_t)Tg * words);  // MEMBERS only
 
   if (WRITE) {
     // base of this group: totals of all groups before it
@@ -196,57 +217,43 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
   }
 
   const uint2 *fb = boxes + (size_t)b * N;
-  // the boxes of a chunk are loaded all at once, one chunk ahead, so the
-  // loads of the next chunk are in flight while this one is binned
-  constexpr int kPer = kMaxChunk / kBinThreads;
-  uint2 nxt[kPer];
-  auto load_chunk = [&](int c) {
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kBinThreads;
-      nxt[k] = (i < NC && c + i < N) ? fb[c + i] : make_uint2(kEmptyBox, kEmptyBox);
-    }
+
+  // Column j of the chunk holds box bx: set its bits in the band's tiles.
+  auto set_bits = [&](int j, uint2 bx) {
+    const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
+    const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
+    if (x0 > x1) return;
+    const int ux0 = x0 >> kTileShiftX, ux1 = x1 >> kTileShiftX;
+    const int uy0 = max(y0 >> kTileShiftY, ty0), uy1 = min(y1 >> kTileShiftY, ty0 + ah - 1);
+    const unsigned int bit = 1u << (j & 31);
+    const int wi = j >> 5;
+    for (int ty = uy0; ty <= uy1; ++ty)
+      for (int tx = ux0; tx <= ux1; ++tx)
+        atomicOr(&bits[((ty - ty0) * nTx + tx) * words + wi], bit);
   };
-  load_chunk(0);
-  for (int c0 = 0; c0 < N; c0 += NC) {
-    uint2 cur[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) cur[k] = nxt[k];
-    for (int w = tid; w < Tg * words; w += kBinThreads) bits[w] = 0u;
-    __syncthreads();
-    if (c0 + NC < N) load_chunk(c0 + NC);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kBinThreads;
-      const uint2 bx = cur[k];
-      int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
-      int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
-      if (x0 > x1) continue;
-      int ux0 = x0 >> kTileShiftX, ux1 = x1 >> kTileShiftX;
-      int uy0 = max(y0 >> kTileShiftY, ty0), uy1 = min(y1 >> kTileShiftY, ty0 + ah - 1);
-      const unsigned int bit = 1u << (i & 31);
-      const int wi = i >> 5;
-      for (int ty = uy0; ty <= uy1; ++ty)
-        for (int tx = ux0; tx <= ux1; ++tx)
-          atomicOr(&bits[((ty - ty0) * nTx + tx) * words + wi], bit);
-    }
-    __syncthreads();
-    // compaction: a wave owns tiles wave, wave + 8, ...
+  // Compaction of the first `used` bit words of every tile row (a wave owns
+  // every eighth tile from its own index on), which it leaves cleared;
+  // column j maps to Gaussian col(j).
+  auto compact = [&](int used, auto col) {
     for (int lt = wave; lt < Tg; lt += kBinThreads / kWave) {
       int run = base[lt];
-      const unsigned int *row = bits + (size_t)lt * words;
-      for (int seg = 0; seg < words; seg += 2 * kWave) {
-        int w0 = seg + 2 * lane;
+      unsigned int *row = bits + (size_t)lt * words;
+      for (int seg = 0; seg < used; seg += 2 * kWave) {
+        const int w0 = seg + 2 * lane;  // words even: w0 + 1 < words
         unsigned long long m = 0ull;
-        if (w0 < words) m = (unsigned long long)row[w0] | ((unsigned long long)row[w0 + 1] << 32);
-        int cnt = __popcll(m);
-        int incl = wave_incl_scan(cnt);
+        if (w0 < used) {
+          m = (unsigned long long)row[w0] | ((unsigned long long)row[w0 + 1] << 32);
+          row[w0] = 0u;
+          row[w0 + 1] = 0u;
+        }
+        const int c = __popcll(m);
+        const int incl = wave_incl_scan(c);
         if (WRITE) {
-          int pos = run + incl - cnt;
-          int nb = c0 + w0 * 32;
+          int pos = run + incl - c;
+          const int nb = w0 * 32;
           while (m) {
-            int k = __ffsll((long long)m) - 1;
-            list[pos++] = nb + k;
+            const int k = __ffsll((long long)m) - 1;
+            list[pos++] = col(nb + k);
             m &= m - 1ull;
           }
         }
@@ -254,8 +261,93 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
       }
       if (lane == 0) base[lt] = run;
     }
-    __syncthreads();
+  };
+
+  for (int w = tid; w < Tg * words; w += kBinThreads) bits[w] = 0u;
+
+  if constexpr (!MEMBERS) {
+    // chunks of NC consecutive Gaussians, loaded all at once one chunk ahead
+    constexpr int kPer = kMaxChunk / kBinThreads;
+    uint2 nxt[kPer];
+    auto load_chunk = [&](int c) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kBinThreads;
+        nxt[k] = (i < NC && c + i < N) ? fb[c + i] : make_uint2(kEmptyBox, kEmptyBox);
+      }
+    };
+    load_chunk(0);
+    for (int c0 = 0; c0 < N; c0 += NC) {
+      uint2 cur[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) cur[k] = nxt[k];
+      __syncthreads();  // bits clear
+      if (c0 + NC < N) load_chunk(c0 + NC);
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) set_bits(tid + k * kBinThreads, cur[k]);
+      __syncthreads();
+      compact(min(NC, N - c0 + 31) >> 5, [&](int j) { return c0 + j; });
+    }
+  } else {
+    // the members [0, cnt) form a chunk
+    auto flush = [&](int cnt) {
+      __syncthreads();  // member list complete, bits clear
+      for (int j = tid; j < cnt; j += kBinThreads) set_bits(j, fb[mem[j]]);
+      __syncthreads();
+      compact((cnt + 31) >> 5, [&](int j) { return mem[j]; });
+      __syncthreads();  // the member list is refilled next
+    };
+    const int S = min(NC, kSegSlots * kBinThreads);  // boxes per segment
+    uint2 nxt[kSegSlots];
+    auto load_seg = [&](int s0) {
+#pragma unroll
+      for (int k = 0; k < kSegSlots; ++k) {
+        const int o = k * kBinThreads + tid;
+        nxt[k] = (o < S && s0 + o < N) ? fb[s0 + o] : make_uint2(kEmptyBox, kEmptyBox);
+      }
+    };
+    load_seg(0);
+    int cnt = 0;  // members gathered for the current chunk (uniform)
+    for (int s0 = 0; s0 < N; s0 += S) {
+      bool in[kSegSlots];
+      unsigned long long bal[kSegSlots];
+#pragma unroll
+      for (int k = 0; k < kSegSlots; ++k) {
+        const uint2 bx = nxt[k];
+        const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
+        const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
+        in[k] = x0 <= x1 && (y0 >> kTileShiftY) < ty0 + ah && (y1 >> kTileShiftY) >= ty0;
+        bal[k] = __builtin_amdgcn_ballot_w64(in[k]);
+        if (lane == 0) wcnt[k][wave] = __popcll(bal[k]);
+      }
+      if (s0 + S < N) load_seg(s0 + S);
+      __syncthreads();
+      // members of this segment, in index order (slot-major, then wave, lane)
+      int total = 0, before[kSegSlots];
+#pragma unroll
+      for (int k = 0; k < kSegSlots; ++k) {
+        int wsum = 0, wpre = 0;
+        for (int w = 0; w < kBinThreads / kWave; ++w) {
+          wpre += w < wave ? wcnt[k][w] : 0;
+          wsum += wcnt[k][w];
+        }
+        before[k] = total + wpre;
+        total += wsum;
+      }
+      if (cnt + total > NC) {  // total <= S <= NC
+        flush(cnt);
+        cnt = 0;
+      }
+      const unsigned long long lt_mask = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int k = 0; k < kSegSlots; ++k)
+        if (in[k]) mem[cnt + before[k] + __popcll(bal[k] & lt_mask)] = s0 + k * kBinThreads + tid;
+      cnt += total;
+      __syncthreads();  // wcnt is rewritten by the next segment
+    }
+    if (cnt > 0) flush(cnt);
   }
+  __syncthreads();
   if (!WRITE) {
     long long part = 0;
     for (int lt = tid; lt < Tg; lt += kBinThreads) {
@@ -270,18 +362,19 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
 // ----------------------------------------------------------------------------
 // host launchers
 
-// Tile groups: bands of whole tile rows whose bit rows (Tg x NC bits) fit
-// the LDS budget; within that, frames are split into more bands so that the
-// grid has about kBinTargetGroups workgroups (every band rescans the frame's
-// boxes, which stay in L2).
-static void choose_groups(int B, int N, int nTx, int nTy, int *gh, int *NC) {
+// Tile groups: bands of whole tile rows whose bit rows (Tg x NC bits) -- and,
+// with a member list, its NC indices -- fit the LDS budget; within that,
+// frames are split into more bands so that the grid has about
+// kBinTargetGroups workgroups (every band scans the frame's boxes, which
+// stay in L2).  Integer arithmetic throughout: NC must be a multiple of 64.
+static void choose_groups(int B, int N, int nTx, int nTy, bool members, int *gh, int *NC) {
   long long nc = ((long long)N + 63) / 64 * 64;
   if (nc > kMaxChunk) nc = kMaxChunk;
-  const long long bits = kBinLdsBytes * 8LL;
-  const long long row_max = bits / nTx / 64 * 64;  // a full tile row must fit
+  // one column of a full tile row costs nTx bits, plus 32 for its member index
+  const long long row_max = kBinLdsBytes * 8 / (nTx + (members ? 32 : 0)) / 64 * 64;
   if (nc > row_max) nc = row_max;
   *NC = (int)nc;
-  long long rows = bits / (nc * nTx);
+  long long rows = (kBinLdsBytes - (members ? nc * 4 : 0)) * 8 / (nc * nTx);
   if (rows > kMaxGroupTiles / nTx) rows = kMaxGroupTiles / nTx;
   if (rows > nTy) rows = nTy;
   int want = (int)((kBinTargetGroups + B - 1) / B);  // bands per frame for a full grid
@@ -316,19 +409,31 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   int *gtot = (int *)(w + L.gtot);
   long long BN = (long long)B * N;
   int nTx = (W + kTileW - 1) / kTileW, nTy = (H + kTileH - 1) / kTileH;
-  launch_preprocess(params, B, N, H, W, C, radius, ws, L, stamp_valid, st);
+  const hipError_t pe = launch_preprocess(params, B, N, H, W, C, radius, ws, L, stamp_valid, st);
+  if (pe != hipSuccess) return pe;
   int gh, NC;
-  choose_groups(B, N, nTx, nTy, &gh, &NC);
+  choose_groups(B, N, nTx, nTy, false, &gh, &NC);
+  // Member lists pay when a frame has many bands (a band meets a small share
+  // of its boxes) and the consecutive chunks' compaction is long: every
+  // group compacts N * Tg / 32 bit words, which the member lists cut to the
+  // band's share.  Measured on MI355X: 26% faster binning at 16 bands and
+  // N * Tg = 2^22, a tie at 32 bands and 2^18, slower below.
+  bool members = kBinMembers > 0;
+  if (kBinMembers < 0)
+    members = (nTy + gh - 1) / gh >= kBinMemberBands && (long long)N * nTx * gh >= kBinMemberWords * 32;
+  if (members) choose_groups(B, N, nTx, nTy, true, &gh, &NC);
+  if (NC < 64 || NC % 64 != 0) return hipErrorInvalidValue;  // whole 64-column words per tile row
   int G = (nTy + gh - 1) / gh;
-  size_t lds = (size_t)nTx * gh * (NC / 32) * 4;
+  size_t lds = (size_t)nTx * gh * (NC / 32) * 4 + (members ? (size_t)NC * 4 : 0);
   dim3 grid((unsigned)xcd_grid(G, B));
+  auto k_count = members ? k_bin<false, true> : k_bin<false, false>;
+  auto k_write = members ? k_bin<true, true> : k_bin<true, false>;
   PDR_TIMED(PDR_K_BIN_COUNT, st,
-            hipLaunchKernelGGL(k_bin<false>, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx,
-                               nTy, gh, G, NC, counts, gtot, (int *)nullptr, (int *)nullptr, cap,
-                               hdr));
+            hipLaunchKernelGGL(k_count, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,
+                               gh, G, NC, counts, gtot, (int *)nullptr, (int *)nullptr, cap, hdr));
   PDR_TIMED(PDR_K_BIN_WRITE, st,
-            hipLaunchKernelGGL(k_bin<true>, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx,
-                               nTy, gh, G, NC, counts, gtot, tile_off, list, cap, hdr));
+            hipLaunchKernelGGL(k_write, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,
+                               gh, G, NC, counts, gtot, tile_off, list, cap, hdr));
   return hipGetLastError();
 }
 

@@ -23,7 +23,13 @@ constexpr long long kMaxChunk = 4096;   // Gaussians per binning chunk (bit-matr
 #define PDR_BIN_TARGET_GROUPS 2048
 #endif
 constexpr long long kBinTargetGroups = PDR_BIN_TARGET_GROUPS;  // binning workgroups to aim for
-constexpr long long kBinLdsBytes = 60 * 1024;  // + 4 KB of static bases stays within 64 KB
+constexpr long long kBinLdsBytes = 60 * 1024 - 512;  // + 4.2 KB of static arrays stays within 64 KB
+#ifndef PDR_BIN_MEMBERS
+#define PDR_BIN_MEMBERS -1
+#endif
+constexpr int kBinMembers = PDR_BIN_MEMBERS;  // chunks of band members: -1 auto, 0 never, 1 always
+constexpr int kBinMemberBands = 8;            // auto: member lists from this many bands per frame
+constexpr long long kBinMemberWords = 1 << 14;  // ... and this many bit words compacted per group
 
 // K1 + count + scan + list write; tile_off/list may be the workspace's own
 // regions or caller buffers (inspection entry point, stamp_valid = false so

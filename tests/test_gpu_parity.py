@@ -51,6 +51,16 @@ def test_small_parity(orc, case):
     print(case, res)
 
 
+def test_member_chunks(orc):
+    # a tall ragged frame (10 tile bands) with many Gaussians: binning forms
+    # its chunks from each band's members, several chunks per band
+    B, N, H, W, C = 1, 60000, 150, 420, 1
+    p, g = workloads.make_custom(B, N, H, W, C, seed=12, s_range=(0.5, 6.0), mean_margin=4.0)
+    n = check_lists(orc, p, H, W)
+    res = check_against_oracle(orc, p, g, H, W)
+    print("pairs", n, res)
+
+
 @pytest.mark.parametrize("radius", [1.0, 2.0, 4.5, 12.0])
 def test_radius_variants(orc, radius):
     p, g = workloads.make_custom(2, 80, 40, 48, 2, seed=11, s_range=(0.5, 5.0), mean_margin=6.0)
