@@ -8,8 +8,9 @@
 // the tile and share one LDS staging area: batches of
 // the tile's Gaussian list (record + amplitudes) are loaded cooperatively,
 // then every wave reads them back one by one (broadcast).  For each Gaussian
-// a wave skips, with scalar branches, its units the Gaussian's pixel box
-// misses.
+// a wave skips, with scalar branches, its units that the Gaussian's pixel
+// box misses or that its truncated ellipse provably misses (decided once per
+// entry at staging).
 //
 // Per (Gaussian, pixel): z = L (p - mu) with L the whitening rows scaled by
 // sqrt(log2(e)/2), q' = z1^2 + z2^2, w = exp2(-q') if q' <= k^2 log2(e)/2.
@@ -49,8 +50,8 @@ struct WaveLayout {
 // (so that p - mu is formed from small tile-local numbers: exact for pixels
 // near the mean; folding mu into an offset c = -L mu instead cancels
 // catastrophically for tiny Gaussians, whose L is large), the mask of tile
-// units the pixel box meets, the element offset of the Gaussian's parameter
-// row, and its amplitudes.
+// units the truncated ellipse may meet, the element offset of the Gaussian's
+// parameter row, and its amplitudes.
 template <int CP>
 struct alignas(16) Entry {
   float l11, l12, l21, l22;
@@ -60,14 +61,44 @@ struct alignas(16) Entry {
   float amp[(CP + 3) / 4 * 4];
 };
 
+// Conservative test that no pixel centre of a unit lies inside the
+// truncated ellipse, as the rasters decide it.  With d = p - mu ranging over
+// the rectangle [X0, X1] x [Y0, Y1] of the unit's pixel centres,
+// q'(d) = |L d|^2 = A dx^2 + 2 Bc dx dy + Cc dy^2 is convex, so its minimum
+// over the rectangle is 0 if the rectangle holds d = 0 and otherwise lies on
+// an edge, where it is the clamped minimum of a 1-D quadratic (iA = 1/A,
+// iC = 1/Cc).  An inexact minimiser only raises q' to second order; the unit
+// is dropped only if the minimum exceeds thr by a margin of 1e-4 (thr + m2),
+// m2 = ((|l11| + |l12|)^2 + (|l21| + |l22|)^2) max|d|^2 bounding the squared
+// magnitudes of the terms, which covers the fp32 rounding here and in the
+// rasters' own q' (a few ulp of those terms).
+struct EllipseRows {
+  float l11, l12, l21, l22, A, Bc, Cc, iA, iC, r2;
+};
+__device__ __forceinline__ bool unit_missed(const EllipseRows &E, float X0, float X1, float Y0,
+                                            float Y1, float thr) {
+  if (X0 <= 0.f && X1 >= 0.f && Y0 <= 0.f && Y1 >= 0.f) return false;
+  auto qat = [&](float x, float y) { return (E.A * x) * x + (2.f * E.Bc * x) * y + (E.Cc * y) * y; };
+  // edges y = Y0, Y1 (minimise over x), then x = X0, X1 (over y)
+  const float xa = fminf(fmaxf(-E.Bc * Y0 * E.iA, X0), X1);
+  const float xb = fminf(fmaxf(-E.Bc * Y1 * E.iA, X0), X1);
+  const float ya = fminf(fmaxf(-E.Bc * X0 * E.iC, Y0), Y1);
+  const float yb = fminf(fmaxf(-E.Bc * X1 * E.iC, Y0), Y1);
+  const float qmin = fminf(fminf(qat(xa, Y0), qat(xb, Y1)), fminf(qat(X0, ya), qat(X1, yb)));
+  const float dm = fmaxf(fmaxf(fabsf(X0), fabsf(X1)), fmaxf(fabsf(Y0), fabsf(Y1)));
+  return qmin > thr + 1e-4f * (thr + E.r2 * dm * dm);
+}
+
 // One list entry per thread of the workgroup (computed here, in parallel,
-// so that the per-entry loop only reads and tests bits).
+// so that the per-entry loop only reads and tests bits).  The unit mask
+// holds the units the pixel box meets, less those the truncated ellipse
+// misses.
 template <int CP, int UW>
 __device__ __forceinline__ void stage_entry(Entry<CP> *s, const GRec *__restrict__ recs,
                                             const float *__restrict__ params,
                                             const int *__restrict__ list, int s0, int cnt,
                                             size_t gbase, int P, int c0, int cc, int tid,
-                                            int tx0, int ty0) {
+                                            int tx0, int ty0, float thr) {
   constexpr int UH = kWave / UW, NUX = kTileW / UW, NUY = kTileH / UH;
   if (tid < cnt) {
     const int n = list[s0 + tid];
@@ -93,6 +124,22 @@ __device__ __forceinline__ void stage_entry(Entry<CP> *s, const GRec *__restrict
 #pragma unroll
     for (int j = 0; j < NUY; ++j)
       if (j >= uy0 && j <= uy1) m |= rowm << (j * NUX);
+    EllipseRows E;
+    E.l11 = e.l11; E.l12 = e.l12; E.l21 = e.l21; E.l22 = e.l22;
+    E.A = e.l11 * e.l11 + e.l21 * e.l21;
+    E.Bc = e.l11 * e.l12 + e.l21 * e.l22;
+    E.Cc = e.l12 * e.l12 + e.l22 * e.l22;
+    E.iA = __builtin_amdgcn_rcpf(E.A);
+    E.iC = __builtin_amdgcn_rcpf(E.Cc);
+    const float r1 = fabsf(e.l11) + fabsf(e.l12), r2 = fabsf(e.l21) + fabsf(e.l22);
+    E.r2 = r1 * r1 + r2 * r2;
+    for (int u = 0; u < NUX * NUY; ++u) {
+      if (!(m & (1u << u))) continue;
+      const float X0 = (float)((u % NUX) * UW) + 0.5f - e.mx;
+      const float Y0 = (float)((u / NUX) * UH) + 0.5f - e.my;
+      if (unit_missed(E, X0, X0 + (float)(UW - 1), Y0, Y0 + (float)(UH - 1), thr))
+        m &= ~(1u << u);
+    }
     e.mask = m;
     s[tid] = e;
   }
@@ -163,7 +210,7 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
-    stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0);
+    stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0, thr);
     __syncthreads();
     for (int e = 0; e < cnt; ++e) {
       const unsigned int um =
@@ -310,7 +357,7 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
-    stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0);
+    stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0, thr);
     __syncthreads();
     for (int e = 0; e < cnt; ++e) {
       const unsigned int um =
