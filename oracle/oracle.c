@@ -27,10 +27,27 @@
  * S12 = sum v z1 z2 (derivation: dz1/dtheta = z2 s2/s1, dz2/dtheta =
  * -z1 s1/s2; the truncation indicator is not differentiated).
  *
- * Truncation ties: a pair with |q - k^2| <= tau k^2 may legitimately fall on
- * either side in another precision, so every output also gets a "slack" = the
- * summed absolute value of such pairs' terms, and a "magnitude" = the summed
- * absolute value of all its terms (the scale a relative error refers to).
+ * Truncation ties: a pair with |q - k^2| <= tau k^2 + e_q may legitimately
+ * fall on either side in another precision, so every output also gets a
+ * "slack" = the summed absolute value of such pairs' terms, and a
+ * "magnitude" = the summed absolute value of all its terms (the scale a
+ * relative error refers to).
+ *
+ * Single-precision allowance (the pages fix no precision; this bounds what an
+ * fp32 evaluation of the definition above can reach).  Rounding p - mu (from a
+ * tile-local fp32 mean), the rotation/scale rows and their products gives z1,
+ * z2 absolute errors that scale with |p - mu| / s, not with |z|: for a thin
+ * Gaussian whose whitened coordinate cancels to near zero the relative error
+ * of z, and of every term built from it, is unbounded.  With u = 2^-24, per
+ * pair
+ *   e_d  = u (2 |d| + 16)                                    (dx and dy)
+ *   e_z1 = (|c| e_dx + |s| e_dy + 3u (|c dx| + |s dy|)) / s1
+ *   e_z2 = (|s| e_dx + |c| e_dy + 3u (|s dx| + |c dy|)) / s2
+ *   e_q  = 2 (|z1| e_z1 + |z2| e_z2) + 3u q,   e_w = w (e_q / 2 + 2u)
+ * e_q widens the tie band, and with the cond flag every pair inside the
+ * truncation adds the first-order error of its terms to the slack:
+ * |a| e_w (image), |G| e_w (dL/da), and for the five sums |h|_1 (e_w |t| +
+ * w e_t), e_t the error the factors z contribute to the term t / v.
  *
  * Binning: per Gaussian the pixel bounding box of the ellipse q <= k^2,
  *   ex = k sqrt((s1 c)^2 + (s2 s)^2),  ey = k sqrt((s1 s)^2 + (s2 c)^2)
@@ -100,6 +117,18 @@ static double pixel_q(const gauss_geo *G, int x, int y, double *z1, double *z2) 
     return (*z1) * (*z1) + (*z2) * (*z2);
 }
 
+/* single-precision allowance of one pair (see the header) */
+#define U32 5.9604644775390625e-08 /* 2^-24 */
+static void pair_err(const gauss_geo *G, int x, int y, double z1, double z2, double q,
+                     double *ez1, double *ez2, double *eq) {
+    double dx = (x + 0.5) - G->mx, dy = (y + 0.5) - G->my;
+    double edx = U32 * (2.0 * fabs(dx) + 16.0), edy = U32 * (2.0 * fabs(dy) + 16.0);
+    double ac = fabs(G->c), as = fabs(G->s);
+    *ez1 = (ac * edx + as * edy + 3.0 * U32 * (fabs(G->c * dx) + fabs(G->s * dy))) / G->s1;
+    *ez2 = (as * edx + ac * edy + 3.0 * U32 * (fabs(G->s * dx) + fabs(G->c * dy))) / G->s2;
+    *eq = 2.0 * (fabs(z1) * (*ez1) + fabs(z2) * (*ez2)) + 3.0 * U32 * q;
+}
+
 /* the scan box: the pixel box enlarged by one pixel, so that pairs sitting
  * just outside the box with q within the tie band still get slack */
 static int scan_box(const gauss_geo *G, int H, int W, int *xa, int *xb, int *ya, int *yb) {
@@ -152,6 +181,7 @@ typedef struct {
     const double *params;
     int N, H, W, C, allpairs;
     double k, tau;
+    int cond;
     double *image, *slack, *mag;
     long long *pairs;
 } fwd_ctx;
@@ -162,15 +192,18 @@ static void fwd_pair(const fwd_ctx *F, const double *g, const gauss_geo *G, int 
     double q = pixel_q(G, x, y, &z1, &z2);
     double kk = F->k * F->k;
     double e = exp(-0.5 * q);
+    double ez1, ez2, eq;
+    pair_err(G, x, y, z1, z2, q, &ez1, &ez2, &eq);
     size_t pix = ((size_t)y * F->W + x) * F->C;
     if (q <= kk) {
         (*npairs)++;
         for (int ch = 0; ch < F->C; ch++) {
             img[pix + ch] += g[5 + ch] * e;
             if (mg) mg[pix + ch] += fabs(g[5 + ch]) * e;
+            if (slk && F->cond) slk[pix + ch] += fabs(g[5 + ch]) * e * (0.5 * eq + 2.0 * U32);
         }
     }
-    if (slk && fabs(q - kk) <= F->tau * kk)
+    if (slk && fabs(q - kk) <= F->tau * kk + eq)
         for (int ch = 0; ch < F->C; ch++) slk[pix + ch] += fabs(g[5 + ch]) * e;
 }
 
@@ -210,10 +243,10 @@ static void fwd_frame(void *p, int b) {
 
 /* image/slack/mag: [B][H][W][C] fp64 (slack, mag, pairs may be NULL) */
 int orc_render(const double *params, int B, int N, int H, int W, int C, double k, double tau,
-               int allpairs, int nthreads, double *image, double *slack, double *mag,
+               int cond, int allpairs, int nthreads, double *image, double *slack, double *mag,
                long long *pairs) {
     if (!params || !image || B < 1 || N < 0 || H < 1 || W < 1 || C < 1) return -1;
-    fwd_ctx F = {params, N, H, W, C, allpairs, k, tau, image, slack, mag, pairs};
+    fwd_ctx F = {params, N, H, W, C, allpairs, k, tau, cond, image, slack, mag, pairs};
     for_frames(B, nthreads, fwd_frame, &F);
     return 0;
 }
@@ -225,6 +258,7 @@ typedef struct {
     const double *params, *grad_image;
     int N, H, W, C;
     double k, tau;
+    int cond;
     double *grad, *gslack, *gmag;
 } bwd_ctx;
 
@@ -256,8 +290,10 @@ static void bwd_frame(void *p, int b) {
             for (int x = xa; x <= xb; x++) {
                 double z1, z2;
                 double q = pixel_q(&G, x, y, &z1, &z2);
+                double ez1, ez2, eq;
+                pair_err(&G, x, y, z1, z2, q, &ez1, &ez2, &eq);
                 int inside = q <= kk;
-                int tie = fabs(q - kk) <= Bc->tau * kk;
+                int tie = fabs(q - kk) <= Bc->tau * kk + eq;
                 if (!inside && !tie) continue;
                 double e = exp(-0.5 * q);
                 const double *gpx = gi + ((size_t)y * W + x) * C;
@@ -278,6 +314,17 @@ static void bwd_frame(void *p, int b) {
                 for (int j = 0; j < 5; j++) {
                     if (inside) { S[C + j] += term[j]; M[C + j] += tabs[j]; }
                     if (tie) Z[C + j] += tabs[j];
+                }
+                if (inside && Bc->cond) {
+                    /* first-order single-precision error of each term */
+                    double ew = e * (0.5 * eq + 2.0 * U32);
+                    double a1 = fabs(z1), a2 = fabs(z2);
+                    double et[5] = {ew * a1 + e * ez1, ew * a2 + e * ez2,
+                                    ew * z1 * z1 + 2.0 * e * a1 * ez1,
+                                    ew * z2 * z2 + 2.0 * e * a2 * ez2,
+                                    ew * a1 * a2 + e * (a2 * ez1 + a1 * ez2)};
+                    for (int ch = 0; ch < C; ch++) Z[ch] += fabs(gpx[ch]) * ew;
+                    for (int j = 0; j < 5; j++) Z[C + j] += habs * et[j];
                 }
             }
         }
@@ -307,9 +354,10 @@ static void bwd_frame(void *p, int b) {
 
 /* grad/gslack/gmag: [B][N][5+C] fp64 (gslack, gmag may be NULL) */
 int orc_grad(const double *params, const double *grad_image, int B, int N, int H, int W, int C,
-             double k, double tau, int nthreads, double *grad, double *gslack, double *gmag) {
+             double k, double tau, int cond, int nthreads, double *grad, double *gslack,
+             double *gmag) {
     if (!params || !grad_image || !grad || B < 1 || N < 0 || H < 1 || W < 1 || C < 1) return -1;
-    bwd_ctx Bc = {params, grad_image, N, H, W, C, k, tau, grad, gslack, gmag};
+    bwd_ctx Bc = {params, grad_image, N, H, W, C, k, tau, cond, grad, gslack, gmag};
     for_frames(B, nthreads, bwd_frame, &Bc);
     return 0;
 }

@@ -102,6 +102,25 @@ def test_tiny_gaussians(orc):
     check_against_oracle(orc, p, g, H, W)
 
 
+@pytest.mark.parametrize("radius", [1.0, 3.0])
+def test_needles_near_unit_corners(orc, radius):
+    # long thin rotated Gaussians: their pixel boxes meet many 8x8 units that
+    # the ellipse itself misses, and with means on and near unit corners the
+    # ellipse grazes unit edges (the rasters' per-unit culling must keep every
+    # unit holding a pixel inside the truncation)
+    rng = np.random.default_rng(33)
+    B, N, H, W, C = 2, 150, 72, 88, 3
+    p, g = workloads.make_custom(B, N, H, W, C, seed=33)
+    p[:, :, 0] = rng.integers(0, W // 8 + 1, (B, N)) * 8 + rng.choice([0.0, 0.5, 1e-3, -0.3], (B, N))
+    p[:, :, 1] = rng.integers(0, H // 8 + 1, (B, N)) * 8 + rng.choice([0.0, 0.5, -1e-3, 0.3], (B, N))
+    p[:, :, 2] = rng.uniform(8.0, 40.0, (B, N))
+    p[:, :, 3] = np.exp(rng.uniform(np.log(0.05), np.log(0.6), (B, N)))
+    p[:, :, 4] = rng.uniform(0.0, np.pi, (B, N))
+    p[:, ::7, 4] = np.pi / 4   # exact diagonals
+    check_lists(orc, p, H, W, radius)
+    check_against_oracle(orc, p, g, H, W, radius)
+
+
 def test_single_gaussian_closed_form():
     # GPU vs the closed form a 2 pi s1 s2 of an untruncated Gaussian (fp32)
     H = W = 96
