@@ -29,6 +29,8 @@
 // steps every lane holds one total; one global fp32 atomic per wave per
 // Gaussian per sum lands in grad_params, and a finalise kernel applies the
 // chain rule in place.
+#include <type_traits>
+
 #include "pdr_common.hpp"
 #include "pdr_internal.hpp"
 
@@ -212,11 +214,14 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
     __syncthreads();
     stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0, thr);
     __syncthreads();
-    for (int e = 0; e < cnt; ++e) {
-      const unsigned int um =
-          (__builtin_amdgcn_readfirstlane(s[e].mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
-      if (um == 0u) continue;
+    // the entry loop runs on a scalar count; each entry is read whole (its
+    // unit mask is all but never empty for a listed Gaussian)
+    const int ecnt = __builtin_amdgcn_readfirstlane(cnt);
+    for (int e = 0; e < ecnt; ++e) {
       const Entry<CP> r = s[e];
+      const unsigned int um =
+          (__builtin_amdgcn_readfirstlane(r.mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+      if (um == 0u) continue;
       float a[CP];
 #pragma unroll
       for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
@@ -297,6 +302,33 @@ __device__ __forceinline__ int value_index(int lane) {
   return idx;
 }
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Calls fn(IC<u>, IC<1>) for the lowest unit u of the mask um (non-empty),
+// then fn(IC<v>, IC<0>) for every later unit v in um, each with its index
+// known at compile time.
+template <int U, int NU, class Fn>
+__device__ __forceinline__ void for_units_after(unsigned int um, Fn &fn) {
+  if constexpr (U < NU) {
+    if (um & (1u << U)) fn(IC<U>{}, IC<0>{});
+    for_units_after<U + 1, NU>(um, fn);
+  }
+}
+template <int NU, int F = 0, class Fn>
+__device__ __forceinline__ void for_units_from_first(unsigned int um, Fn &fn) {
+  if constexpr (F < NU - 1) {
+    if (um & (1u << F)) {
+      fn(IC<F>{}, IC<1>{});
+      for_units_after<F + 1, NU>(um, fn);
+    } else {
+      for_units_from_first<NU, F + 1>(um, fn);
+    }
+  } else {
+    fn(IC<F>{}, IC<1>{});
+  }
+}
+
 template <int K>
 struct Pow2Up {
   static constexpr int value = K <= 8 ? 8 : (K <= 16 ? 16 : 32);
@@ -359,47 +391,61 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
     __syncthreads();
     stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0, thr);
     __syncthreads();
-    for (int e = 0; e < cnt; ++e) {
-      const unsigned int um =
-          (__builtin_amdgcn_readfirstlane(s[e].mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
-      if (um == 0u) continue;
+    // the entry loop runs on a scalar count; each entry is read whole (its
+    // unit mask is all but never empty for a listed Gaussian)
+    const int ecnt = __builtin_amdgcn_readfirstlane(cnt);
+    for (int e = 0; e < ecnt; ++e) {
       const Entry<CP> r = s[e];
+      const unsigned int um =
+          (__builtin_amdgcn_readfirstlane(r.mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+      if (um == 0u) continue;
       float a[CP];
 #pragma unroll
       for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
+      // The first unit of the mask assigns the partial sums (no zeroing);
+      // the later ones add to them and are skipped when no lane of the unit
+      // lies inside the truncation.
       float part[KP];
 #pragma unroll
-      for (int k = 0; k < KP; ++k) part[k] = 0.f;
+      for (int k = K; k < KP; ++k) part[k] = 0.f;
       bool any = false;
-#pragma unroll
-      for (int j = 0; j < UY; ++j) {
-        if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
+      auto unit = [&](auto uc, auto firstc) {
+        constexpr int u = decltype(uc)::value, j = u / UX, i = u % UX;
+        constexpr bool first = decltype(firstc)::value != 0;
         const float dy = (fy + (float)(UH * j)) - r.my;
+        const float dx = (fx + (float)(UW * i)) - r.mx;
+        const float u1 = r.l11 * dx + r.l12 * dy;
+        const float u2 = r.l21 * dx + r.l22 * dy;
+        const float q = u1 * u1 + u2 * u2;
+        const bool inside = q <= thr;
+        const bool hit = __builtin_amdgcn_ballot_w64(inside) != 0ull;
+        if (!first && !hit) return;
+        any |= hit;
+        const float w = inside ? __builtin_amdgcn_exp2f(-q) : 0.f;
+        float h = G[j][i][0] * a[0];
 #pragma unroll
-        for (int i = 0; i < UX; ++i) {
-          if (!(um & (1u << (j * UX + i)))) continue;
-          const float dx = (fx + (float)(UW * i)) - r.mx;
-          const float u1 = r.l11 * dx + r.l12 * dy;
-          const float u2 = r.l21 * dx + r.l22 * dy;
-          const float q = u1 * u1 + u2 * u2;
-          const bool inside = q <= thr;
-          if (__builtin_amdgcn_ballot_w64(inside) == 0ull) continue;
-          any = true;
-          const float w = inside ? __builtin_amdgcn_exp2f(-q) : 0.f;
-          float h = 0.f;
+        for (int c = 1; c < CP; ++c) h += G[j][i][c] * a[c];
+        const float v = h * w;
+        const float t1 = v * u1, t2 = v * u2;
+        if constexpr (first) {
 #pragma unroll
-          for (int c = 0; c < CP; ++c) h += G[j][i][c] * a[c];
-          const float v = h * w;
+          for (int c = 0; c < CP; ++c) part[c] = G[j][i][c] * w;
+          part[CP + 0] = t1;
+          part[CP + 1] = t2;
+          part[CP + 2] = t1 * u1;
+          part[CP + 3] = t2 * u2;
+          part[CP + 4] = t1 * u2;
+        } else {
 #pragma unroll
           for (int c = 0; c < CP; ++c) part[c] += G[j][i][c] * w;
-          const float t1 = v * u1, t2 = v * u2;
           part[CP + 0] += t1;
           part[CP + 1] += t2;
           part[CP + 2] += t1 * u1;
           part[CP + 3] += t2 * u2;
           part[CP + 4] += t1 * u2;
         }
-      }
+      };
+      for_units_from_first<WL::kUnitsPerWave>(um, unit);
       if (!any) continue;
       const float tot = wave_reduce_transposed<KP>(part, lane);
       if (slot >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot), tot);
