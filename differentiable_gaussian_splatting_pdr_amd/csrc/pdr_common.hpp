@@ -99,7 +99,7 @@ inline Layout make_layout(long long BN, long long BT, long long BR, long long ca
 }
 
 // ----------------------------------------------------------------------------
-// wave64 cross-lane helpers (DPP / ds_swizzle / permlane swaps)
+// wave64 cross-lane helpers (DPP / ds_swizzle / ds_bpermute)
 
 // DPP control words (GFX9 encoding).
 constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
@@ -147,18 +147,52 @@ __device__ __forceinline__ float xor_partner(float v) {
   return __int_as_float(x);
 }
 
-// Sum with the partner lane for MASK in {4, 8, 16, 32} (an all-reduce step).
+// Sum with the partner lane (lane ^ MASK, MASK in {1, 2, 4, 8, 16}): an
+// all-reduce step.
 template <int MASK>
 __device__ __forceinline__ float xor_sum(float v) {
-  if constexpr (MASK == 16) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
-    return __int_as_float(r[0]) + __int_as_float(r[1]);
-  } else if constexpr (MASK == 32) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-    return __int_as_float(r[0]) + __int_as_float(r[1]);
-  } else {
-    return v + xor_partner<MASK>(v);
+  return v + xor_partner<MASK>(v);
+}
+
+// One exchange step of the transposed butterfly: lanes with (lane & MASK)
+// keep the upper HALF values, the others the lower HALF, and add the
+// partner's copy of the half they keep.
+template <int HALF, int MASK>
+__device__ __forceinline__ void tstep(float *v, bool up) {
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const float keep = up ? v[i + HALF] : v[i];
+    const float send = up ? v[i] : v[i + HALF];
+    v[i] = keep + xor_partner<MASK>(send);
   }
+}
+
+// Reduce KP per-lane values over the wave.  Afterwards every lane holds the
+// wave total of value index bitrev_log2(KP)(lane & (KP - 1)).
+template <int KP>
+__device__ __forceinline__ float wave_reduce_transposed(float *v, int lane) {
+  static_assert(KP == 8 || KP == 16 || KP == 32, "KP");
+  tstep<KP / 2, 1>(v, lane & 1);
+  tstep<KP / 4, 2>(v, lane & 2);
+  tstep<KP / 8, 4>(v, lane & 4);
+  if constexpr (KP >= 16) tstep<KP / 16, 8>(v, lane & 8);
+  if constexpr (KP >= 32) tstep<KP / 32, 16>(v, lane & 16);
+  float r = v[0];
+  if constexpr (KP < 16) r = xor_sum<8>(r);
+  // the last exchanges through the LDS crossbar (no VALU but the add;
+  // measured faster than the permlane swaps): ds_swizzle for lane ^ 16,
+  // ds_bpermute for lane ^ 32
+  if constexpr (KP < 32) r += xor_partner<16>(r);
+  return r + __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(r)));
+}
+
+template <int KP>
+__device__ __forceinline__ int value_index(int lane) {
+  int idx = 0;
+#pragma unroll
+  for (int s = 0, h = KP / 2; h >= 1; ++s, h >>= 1)
+    if (lane & (1 << s)) idx += h;
+  return idx;
 }
 
 // Blocks of a frame-major grid of (frame, item) are spread so that all items

@@ -264,44 +264,6 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
   }
 }
 
-// One exchange step of the transposed butterfly: lanes with (lane & MASK)
-// keep the upper HALF values, the others the lower HALF, and add the
-// partner's copy of the half they keep.
-template <int HALF, int MASK>
-__device__ __forceinline__ void tstep(float *v, bool up) {
-#pragma unroll
-  for (int i = 0; i < HALF; ++i) {
-    const float keep = up ? v[i + HALF] : v[i];
-    const float send = up ? v[i] : v[i + HALF];
-    v[i] = keep + xor_partner<MASK>(send);
-  }
-}
-
-// Reduce KP per-lane values over the wave.  Afterwards every lane holds the
-// wave total of value index bitrev_log2(KP)(lane & (KP - 1)).
-template <int KP>
-__device__ __forceinline__ float wave_reduce_transposed(float *v, int lane) {
-  static_assert(KP == 8 || KP == 16 || KP == 32, "KP");
-  tstep<KP / 2, 1>(v, lane & 1);
-  tstep<KP / 4, 2>(v, lane & 2);
-  tstep<KP / 8, 4>(v, lane & 4);
-  if constexpr (KP >= 16) tstep<KP / 16, 8>(v, lane & 8);
-  if constexpr (KP >= 32) tstep<KP / 32, 16>(v, lane & 16);
-  float r = v[0];
-  if constexpr (KP < 16) r = xor_sum<8>(r);
-  if constexpr (KP < 32) r = xor_sum<16>(r);
-  return xor_sum<32>(r);
-}
-
-template <int KP>
-__device__ __forceinline__ int value_index(int lane) {
-  int idx = 0;
-#pragma unroll
-  for (int s = 0, h = KP / 2; h >= 1; ++s, h >>= 1)
-    if (lane & (1 << s)) idx += h;
-  return idx;
-}
-
 template <int V>
 using IC = std::integral_constant<int, V>;
 

@@ -66,41 +66,6 @@ __device__ __forceinline__ float load_gb(__amdgpu_buffer_rsrc_t r, uint32_t off)
   }
 }
 
-// One exchange step of the transposed butterfly (lane ^ MASK).
-template <int HALF, int MASK>
-__device__ __forceinline__ void span_tstep(float *v, bool up) {
-#pragma unroll
-  for (int i = 0; i < HALF; ++i) {
-    const float keep = up ? v[i + HALF] : v[i];
-    const float send = up ? v[i] : v[i + HALF];
-    v[i] = keep + xor_partner<MASK>(send);
-  }
-}
-
-// Wave total of KP per-lane values; lane l (l < KP) ends with the total of
-// value index bit-reverse(l) (see span_value_index).
-template <int KP>
-__device__ __forceinline__ float span_reduce(float *v, int lane) {
-  static_assert(KP == 8 || KP == 16 || KP == 32, "KP");
-  span_tstep<KP / 2, 1>(v, lane & 1);
-  span_tstep<KP / 4, 2>(v, lane & 2);
-  span_tstep<KP / 8, 4>(v, lane & 4);
-  if constexpr (KP >= 16) span_tstep<KP / 16, 8>(v, lane & 8);
-  if constexpr (KP >= 32) span_tstep<KP / 32, 16>(v, lane & 16);
-  float r = v[0];
-  if constexpr (KP < 16) r = xor_sum<8>(r);
-  if constexpr (KP < 32) r = xor_sum<16>(r);
-  return xor_sum<32>(r);
-}
-
-template <int KP>
-__device__ __forceinline__ int span_value_index(int lane) {
-  int idx = 0;
-#pragma unroll
-  for (int s = 0, h = KP / 2; h >= 1; ++s, h >>= 1)
-    if (lane & (1 << s)) idx += h;
-  return idx;
-}
 
 template <int K>
 struct SpanPow2 {
@@ -128,7 +93,7 @@ __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
   const float thr_span = thr * (1.0f + kSpanMargin);
   int *st_start = s_start[wv], *st_xs = s_xs[wv], *st_row = s_row[wv];
   float *st_sum = s_sum[wv];
-  const int vidx = span_value_index<KP>(lane & (KP - 1));
+  const int vidx = value_index<KP>(lane & (KP - 1));
 
   for (int j = 0; j < kSpanPerWave; ++j) {
     const int n = item * kSpanPerBlock + j * kSpanWaves + wv;
@@ -256,7 +221,7 @@ __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
         for (int c = 0; c < CP; ++c) G_c[c] = G_n[c];
       }
     }
-    const float tot = span_reduce<KP>(part, lane);
+    const float tot = wave_reduce_transposed<KP>(part, lane);
     if (lane < KP) st_sum[vidx] = tot;
     // the chain rule (fp64), undoing the kappa scale of the whitened rows:
     //   dmu = L^T (S1, S2), ds1 = S11 / s1, ds2 = S22 / s2,
