@@ -147,6 +147,14 @@ __device__ __forceinline__ float xor_partner(float v) {
   return __int_as_float(x);
 }
 
+// DPP row shift: lane i reads lane i + D of its 16-lane row (lanes whose
+// source lies outside the row read 0, bound_ctrl).
+template <int D>
+__device__ __forceinline__ float dpp_row_shl(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + D, 0xF, 0xF, true));
+}
+
 // Sum with the partner lane (lane ^ MASK, MASK in {1, 2, 4, 8, 16}): an
 // all-reduce step.
 template <int MASK>
