@@ -192,8 +192,8 @@ static void fwd_pair(const fwd_ctx *F, const double *g, const gauss_geo *G, int 
     double q = pixel_q(G, x, y, &z1, &z2);
     double kk = F->k * F->k;
     double e = exp(-0.5 * q);
-    double ez1, ez2, eq;
-    pair_err(G, x, y, z1, z2, q, &ez1, &ez2, &eq);
+    double ez1 = 0.0, ez2 = 0.0, eq = 0.0;
+    if (slk) pair_err(G, x, y, z1, z2, q, &ez1, &ez2, &eq); /* only feeds the slack */
     size_t pix = ((size_t)y * F->W + x) * F->C;
     if (q <= kk) {
         (*npairs)++;
@@ -290,10 +290,10 @@ static void bwd_frame(void *p, int b) {
             for (int x = xa; x <= xb; x++) {
                 double z1, z2;
                 double q = pixel_q(&G, x, y, &z1, &z2);
-                double ez1, ez2, eq;
-                pair_err(&G, x, y, z1, z2, q, &ez1, &ez2, &eq);
+                double ez1 = 0.0, ez2 = 0.0, eq = 0.0;
+                if (osl) pair_err(&G, x, y, z1, z2, q, &ez1, &ez2, &eq); /* only feeds the slack */
                 int inside = q <= kk;
-                int tie = fabs(q - kk) <= Bc->tau * kk + eq;
+                int tie = osl && fabs(q - kk) <= Bc->tau * kk + eq;
                 if (!inside && !tie) continue;
                 double e = exp(-0.5 * q);
                 const double *gpx = gi + ((size_t)y * W + x) * C;
@@ -315,7 +315,7 @@ static void bwd_frame(void *p, int b) {
                     if (inside) { S[C + j] += term[j]; M[C + j] += tabs[j]; }
                     if (tie) Z[C + j] += tabs[j];
                 }
-                if (inside && Bc->cond) {
+                if (inside && osl && Bc->cond) {
                     /* first-order single-precision error of each term */
                     double ew = e * (0.5 * eq + 2.0 * U32);
                     double a1 = fabs(z1), a2 = fabs(z2);
