@@ -8,8 +8,11 @@ absolute is the target stated for the fp32 outputs), elementwise:
   grads:  |gpu - ref| <= 1e-5 + 1e-4 mag  + slack
 
 ref is the fp64 oracle; slack is the summed |term| of (Gaussian, pixel) pairs
-within 1e-4 k^2 of the truncation edge (either side is correct there); mag
-is the summed |term| of the output.  A gradient is a sum of up to thousands
+within 1e-4 k^2 (plus the pair's fp32 error bound of q) of the truncation
+edge, where either side is correct, plus each pair's single-precision
+allowance (the first-order fp32 error of its terms, which for thin rotated
+Gaussians is not proportional to the term; oracle header); mag is the
+summed |term| of the output.  A gradient is a sum of up to thousands
 of signed terms, each carrying an fp32 relative error of ~1e-7..1e-6, so its
 error scales with mag, not with the (possibly cancelling) |ref|.
 """
