@@ -24,11 +24,15 @@ ATOL = 1e-5
 RTOL = 1e-4
 
 
-def gpu_forward_backward(params, grad_image, H, W, radius=3.0, reuse=True, algo=None):
+def gpu_forward_backward(params, grad_image, H, W, radius=3.0, reuse=True, algo="tile"):
     """Run forward then backward through the library; numpy in, numpy out.
-    algo: None (library default) or a PDR_BWD_* backward algorithm."""
+    algo: "tile" (the tile raster, whatever the library default would pick
+    for the size), None (the library default) or a PDR_BWD_* value."""
     import torch
-    from differentiable_gaussian_splatting_pdr_amd import splat
+    from differentiable_gaussian_splatting_pdr_amd import _lib, splat
+
+    if algo == "tile":
+        algo = _lib.PDR_BWD_TILE
 
     dev = torch.device("cuda:0")
     p = torch.from_numpy(np.ascontiguousarray(params, dtype=np.float32)).to(dev)

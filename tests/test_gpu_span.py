@@ -122,3 +122,20 @@ def test_span_stale_and_rejects():
                                      wl.W, 17, 3.0, ws.ptr, ws.nbytes, 0, span(), None) == -1
     assert L.pdr_splat_backward_algo(pt.data_ptr(), gt.data_ptr(), 0, gp.data_ptr(), 1, wl.N, wl.H,
                                      wl.W, wl.C, 3.0, ws.ptr, ws.nbytes, 0, 7, None) == -1
+
+
+def test_auto_choice(orc):
+    # the library default takes the span walk for small problems (B*N <= 32768)
+    # and the tile raster beyond; the span walk is deterministic (no atomics),
+    # so the small default result equals the explicit span result bit for bit
+    from differentiable_gaussian_splatting_pdr_amd import _lib
+    p, g = workloads.make_custom(4, 500, 48, 40, 3, seed=61, s_range=(0.5, 6.0), mean_margin=4.0)
+    auto = gpu_forward_backward(p, g, 48, 40, algo=None)["grad"]
+    assert np.array_equal(auto, gpu_forward_backward(p, g, 48, 40, algo=span())["grad"])
+    check_against_oracle(orc, p, g, 48, 40, gpu=gpu_forward_backward(p, g, 48, 40, algo=None))
+    p, g = workloads.make_custom(9, 4000, 32, 32, 1, seed=62, s_range=(0.5, 4.0), mean_margin=2.0)
+    a = gpu_forward_backward(p, g, 32, 32, algo=None)["grad"]
+    t = gpu_forward_backward(p, g, 32, 32, algo=_lib.PDR_BWD_TILE)["grad"]
+    s = gpu_forward_backward(p, g, 32, 32, algo=span())["grad"]
+    assert not np.array_equal(a, s) or np.array_equal(t, s)   # large: not the span walk
+    check_against_oracle(orc, p, g, 32, 32, gpu=gpu_forward_backward(p, g, 32, 32, algo=None))
