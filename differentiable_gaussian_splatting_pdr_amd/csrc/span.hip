@@ -1,10 +1,10 @@
 // span.hip -- tile-free backward: one wave per Gaussian over the compacted
 // pixels of its support.
 //
-// The tile backward evaluates every pixel of every 8x8 unit a Gaussian's box
-// touches (about 43% of those lanes are inside the support on the benchmark
-// workload) and reduces the per-lane partial sums once per (tile, Gaussian)
-// list entry.  Here a wave owns one Gaussian: for every row of its box it
+// The tile backward evaluates every pixel of every 8x8 unit that a
+// Gaussian's truncated ellipse may touch (under half of those lanes are
+// inside the support on the benchmark workload) and reduces the per-lane
+// partial sums once per (tile, Gaussian) list entry.  Here a wave owns one Gaussian: for every row of its box it
 // computes the row's span of pixel centres inside the truncated ellipse
 // (the roots of a quadratic, widened by a relative 1e-3 of the threshold so
 // the span is a superset; the per-pixel test q <= k^2 then decides exactly as
