@@ -13,7 +13,7 @@ using namespace pdr;
 namespace {
 
 struct Dims {
-  long long BN, BT, BR;
+  long long BN, BT;
   int nTx, nTy;
 };
 
@@ -28,7 +28,6 @@ int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
   d->nTy = (H + kTileH - 1) / kTileH;
   d->BN = BN;
   d->BT = (long long)B * d->nTx * d->nTy;
-  d->BR = (long long)B * d->nTy;
   if (d->BT + 1 > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
   return PDR_OK;
 }
@@ -42,11 +41,11 @@ int validate_radius(float radius) {
 int layout_for(const Dims &d, void *ws, size_t bytes, Layout *L) {
   if (!ws) return PDR_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return PDR_ERR_WORKSPACE;
-  Layout fixed = make_layout(d.BN, d.BT, d.BR, 0);
+  Layout fixed = make_layout(d.BN, d.BT, 0);
   if (bytes < fixed.list) return PDR_ERR_WORKSPACE;
   long long cap = (long long)((bytes - fixed.list) / 4);
   if (cap > 0x7fffffffLL) cap = 0x7fffffffLL;
-  *L = make_layout(d.BN, d.BT, d.BR, cap);
+  *L = make_layout(d.BN, d.BT, cap);
   L->total = bytes;
   return PDR_OK;
 }
@@ -146,7 +145,7 @@ long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long
   int rc = validate_sizes(B, N, H, W, C, &d);
   if (rc != PDR_OK) return rc;
   if (max_pairs < 0 || max_pairs > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
-  return (long long)make_layout(d.BN, d.BT, d.BR, max_pairs).total;
+  return (long long)make_layout(d.BN, d.BT, max_pairs).total;
 }
 
 int pdr_splat_forward(const float *params, float *image, int B, int N, int H, int W, int C,

@@ -2,12 +2,14 @@
 //
 //  k_preprocess   one thread per Gaussian: validity, fp64 pixel bounding box
 //                 of the truncated ellipse q <= k^2, whitening rows.
-//  k_bin<false,M> per (frame, tile group): per-tile overlap counts.
-//  k_bin<true,M>  per (frame, tile group): the per-tile lists, ascending
-//                 Gaussian index, at the scanned offsets.
+//  k_bin<false,M,X> per (frame, tile group): per-tile overlap counts.
+//  k_bin<true,M,X>  per (frame, tile group): the per-tile lists, ascending
+//                   Gaussian index, at the scanned offsets.
 //
-// A tile group holds a band of tile rows and walks the frame's Gaussians in
-// chunks (consecutive Gaussians, or, M = true, the band's members); for each
+// A tile group holds a band of tile rows (or, when a batch has too few tile
+// rows to fill the GPU, a column chunk of a one-row band) and walks the
+// frame's Gaussians in chunks (consecutive Gaussians, or, M = true, the
+// group's members); for each
 // chunk it builds an LDS bit matrix [tile][Gaussian] of box overlaps and
 // compacts every tile's bit row with a wave scan.  The lists are thus
 // produced in ascending order with no sort and no global atomics.
@@ -124,9 +126,12 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
   return t;
 }
 
-// LDS bit matrix binning.  Grid: G bands x B frames (1D, XCD-aware); a group is
-// a band of gh whole tile rows.  Dynamic LDS: Tg * (NC / 32) words of bits
-// (NC a multiple of 64), then, with MEMBERS, NC member indices.
+// LDS bit matrix binning.  Grid: G groups x B frames (1D, XCD-aware); a group
+// is a band of gh whole tile rows, or with ncc > 1 column chunks one tile row
+// of cw tiles (the last chunk narrower).  Either way its tiles are one
+// contiguous run of the frame's row-major tile order.  Dynamic LDS:
+// Tg * (NC / 32) words of bits (NC a multiple of 64), then, with MEMBERS, NC
+// member indices.
 //
 // A chunk is a set of at most NC Gaussians in ascending index order; each
 // sets, in its column, the bits of the band's tiles its box overlaps, each
@@ -136,8 +141,8 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
 //  MEMBERS = false  chunk = NC consecutive Gaussians of the frame, loaded one
 //                   chunk ahead; every tile row compacts all NC columns.
 //  MEMBERS = true   the group scans the frame's boxes in segments (loaded one
-//                   segment ahead) and gathers the band's members -- the
-//                   Gaussians whose box meets the band -- into an LDS list in
+//                   segment ahead) and gathers the group's members -- the
+//                   Gaussians whose box meets its tiles -- into an LDS list in
 //                   index order (wave ballots, a prefix over waves); NC
 //                   members form a chunk.  A band then pays for bit setting
 //                   and compaction on its own members only, which wins when
@@ -151,10 +156,10 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
 // total and the overflow flag.  Both passes form the same chunks.
 constexpr int kSegSlots = 4;   // boxes per thread per member-scan segment
 
-template <bool WRITE, bool MEMBERS>
+template <bool WRITE, bool MEMBERS, bool COLS>
 __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ boxes, int B, int N,
-                                                     int nTx, int nTy, int gh, int G, int NC,
-                                                     int *__restrict__ counts,
+                                                     int nTx, int nTy, int gh, int ncc, int cw,
+                                                     int G, int NC, int *__restrict__ counts,
                                                      int *__restrict__ gtot,
                                                      int *__restrict__ tile_off,
                                                      int *__restrict__ list, long long cap,
@@ -164,13 +169,19 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
   __shared__ long long red[kBinThreads / kWave];
   __shared__ int wtot[kBinThreads / kWave];
   __shared__ int wcnt[kSegSlots][kBinThreads / kWave];
-  int b, g;  // frame, band: all bands of a frame on one XCD, so its boxes stay in that L2
+  int b, g;  // frame, group: all groups of a frame on one XCD, so its boxes stay in that L2
   if (!xcd_frame_item(blockIdx.x, G, B, &b, &g)) return;
-  const int ty0 = g * gh;
+  // group g = (band, column chunk): tile rows [ty0, ty0 + ah), tile columns
+  // [cx0, cx0 + aw); with more than one chunk a band is one tile row, so a
+  // group's tiles are always one contiguous run of the frame's tile order
+  const int band = COLS ? g / ncc : g, chunk = COLS ? g - band * ncc : 0;
+  const int ty0 = band * gh;
   const int ah = min(gh, nTy - ty0);
-  const int Tg = nTx * ah;
+  const int cx0 = COLS ? chunk * cw : 0;
+  const int aw = COLS ? min(cw, nTx - cx0) : nTx;
+  const int Tg = aw * ah;
   const int nT = nTx * nTy;
-  const size_t t0 = (size_t)b * nT + (size_t)ty0 * nTx;  // first tile of the group
+  const size_t t0 = (size_t)b * nT + (size_t)ty0 * nTx + cx0;  // first tile of the group
   const int words = NC >> 5;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   unsigned int *bits = dyn;
@@ -223,13 +234,14 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
     const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
     const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
     if (x0 > x1) return;
-    const int ux0 = x0 >> kTileShiftX, ux1 = x1 >> kTileShiftX;
+    const int ux0 = COLS ? max(x0 >> kTileShiftX, cx0) : x0 >> kTileShiftX;
+    const int ux1 = COLS ? min(x1 >> kTileShiftX, cx0 + aw - 1) : x1 >> kTileShiftX;
     const int uy0 = max(y0 >> kTileShiftY, ty0), uy1 = min(y1 >> kTileShiftY, ty0 + ah - 1);
     const unsigned int bit = 1u << (j & 31);
     const int wi = j >> 5;
     for (int ty = uy0; ty <= uy1; ++ty)
       for (int tx = ux0; tx <= ux1; ++tx)
-        atomicOr(&bits[((ty - ty0) * nTx + tx) * words + wi], bit);
+        atomicOr(&bits[((ty - ty0) * aw + (tx - cx0)) * words + wi], bit);
   };
   // Compaction of the first `used` bit words of every tile row (a wave owns
   // every eighth tile from its own index on), which it leaves cleared;
@@ -316,7 +328,8 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
         const uint2 bx = nxt[k];
         const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
         const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
-        in[k] = x0 <= x1 && (y0 >> kTileShiftY) < ty0 + ah && (y1 >> kTileShiftY) >= ty0;
+        in[k] = x0 <= x1 && (y0 >> kTileShiftY) < ty0 + ah && (y1 >> kTileShiftY) >= ty0 &&
+                (!COLS || ((x0 >> kTileShiftX) < cx0 + aw && (x1 >> kTileShiftX) >= cx0));
         bal[k] = __builtin_amdgcn_ballot_w64(in[k]);
         if (lane == 0) wcnt[k][wave] = __popcll(bal[k]);
       }
@@ -365,24 +378,55 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
 // Tile groups: bands of whole tile rows whose bit rows (Tg x NC bits) -- and,
 // with a member list, its NC indices -- fit the LDS budget; within that,
 // frames are split into more bands so that the grid has about
-// kBinTargetGroups workgroups (every band scans the frame's boxes, which
-// stay in L2).  Integer arithmetic throughout: NC must be a multiple of 64.
-static void choose_groups(int B, int N, int nTx, int nTy, bool members, int *gh, int *NC) {
+// kBinTargetGroups workgroups (every group scans the frame's boxes, which
+// stay in L2).  When a whole batch has fewer than kBinChunkBelow tile rows
+// (a few very wide frames), bands are one tile row and are also cut into
+// column chunks of at least kBinMinChunkTiles tiles, aiming at
+// kBinChunkTarget groups: every group still scans all of its frame's boxes,
+// so chunks only pay where a full tile row would force a narrow bit matrix
+// (NC limited by the LDS) and long compactions -- measured on MI355X 290 ->
+// 45 us of binning for one 20 x 16384 frame, but 0.77 -> 7.2 ms for one
+// 2048 x 2048 frame with 262144 Gaussians had the rule chunked it.
+// Integer arithmetic throughout: NC must be a multiple of 64.
+struct BinGroups {
+  int gh;   // tile rows per band
+  int ncc;  // column chunks per band
+  int cw;   // tiles per chunk (the last may be narrower)
+  int NC;   // bit-matrix columns (Gaussians per chunk of the scan)
+  int G;    // groups per frame
+};
+
+static BinGroups choose_groups(int B, int N, int nTx, int nTy, bool members) {
+  BinGroups r;
+  const long long rows_all = (long long)B * nTy;
+  int c = 1;
+  if (rows_all < kBinChunkBelow && nTx >= 2 * kBinMinChunkTiles) {
+    c = (int)((kBinChunkTarget + rows_all - 1) / rows_all);
+    if (c > nTx / kBinMinChunkTiles) c = nTx / kBinMinChunkTiles;
+  }
+  r.cw = (nTx + c - 1) / c;
+  r.ncc = (nTx + r.cw - 1) / r.cw;
   long long nc = ((long long)N + 63) / 64 * 64;
   if (nc > kMaxChunk) nc = kMaxChunk;
-  // one column of a full tile row costs nTx bits, plus 32 for its member index
-  const long long row_max = kBinLdsBytes * 8 / (nTx + (members ? 32 : 0)) / 64 * 64;
+  // one column of a full group row costs cw bits, plus 32 for its member index
+  const long long row_max = kBinLdsBytes * 8 / (r.cw + (members ? 32 : 0)) / 64 * 64;
   if (nc > row_max) nc = row_max;
-  *NC = (int)nc;
-  long long rows = (kBinLdsBytes - (members ? nc * 4 : 0)) * 8 / (nc * nTx);
-  if (rows > kMaxGroupTiles / nTx) rows = kMaxGroupTiles / nTx;
+  r.NC = (int)nc;
+  long long rows = (kBinLdsBytes - (members ? nc * 4 : 0)) * 8 / (nc * r.cw);
+  if (rows > kMaxGroupTiles / r.cw) rows = kMaxGroupTiles / r.cw;
   if (rows > nTy) rows = nTy;
-  int want = (int)((kBinTargetGroups + B - 1) / B);  // bands per frame for a full grid
-  if (want > 1) {
-    int r = (nTy + want - 1) / want;
-    if (r < rows) rows = r;
+  if (r.ncc > 1) {
+    rows = 1;   // chunked bands are single tile rows (contiguous tile runs)
+  } else {
+    int want = (int)((kBinTargetGroups + B - 1) / B);  // bands per frame for a full grid
+    if (want > 1) {
+      int rr = (nTy + want - 1) / want;
+      if (rr < rows) rows = rr;
+    }
   }
-  *gh = rows < 1 ? 1 : (int)rows;
+  r.gh = rows < 1 ? 1 : (int)rows;
+  r.G = (nTy + r.gh - 1) / r.gh * r.ncc;
+  return r;
 }
 
 hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, int C, float radius,
@@ -411,29 +455,32 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   int nTx = (W + kTileW - 1) / kTileW, nTy = (H + kTileH - 1) / kTileH;
   const hipError_t pe = launch_preprocess(params, B, N, H, W, C, radius, ws, L, stamp_valid, st);
   if (pe != hipSuccess) return pe;
-  int gh, NC;
-  choose_groups(B, N, nTx, nTy, false, &gh, &NC);
-  // Member lists pay when a frame has many bands (a band meets a small share
-  // of its boxes) and the consecutive chunks' compaction is long: every
-  // group compacts N * Tg / 32 bit words, which the member lists cut to the
-  // band's share.  Measured on MI355X: 26% faster binning at 16 bands and
-  // N * Tg = 2^22, a tie at 32 bands and 2^18, slower below.
+  BinGroups bg = choose_groups(B, N, nTx, nTy, false);
+  // Member lists pay when a frame has many groups (a group meets a small
+  // share of its boxes) and the consecutive chunks' compaction is long:
+  // every group compacts N * Tg / 32 bit words, which the member lists cut
+  // to the group's share.  Measured on MI355X: 26% faster binning at 16
+  // bands and N * Tg = 2^22, a tie at 32 bands and 2^18, slower below.
   bool members = kBinMembers > 0;
   if (kBinMembers < 0)
-    members = (nTy + gh - 1) / gh >= kBinMemberBands && (long long)N * nTx * gh >= kBinMemberWords * 32;
-  if (members) choose_groups(B, N, nTx, nTy, true, &gh, &NC);
-  if (NC < 64 || NC % 64 != 0) return hipErrorInvalidValue;  // whole 64-column words per tile row
-  int G = (nTy + gh - 1) / gh;
-  size_t lds = (size_t)nTx * gh * (NC / 32) * 4 + (members ? (size_t)NC * 4 : 0);
-  dim3 grid((unsigned)xcd_grid(G, B));
-  auto k_count = members ? k_bin<false, true> : k_bin<false, false>;
-  auto k_write = members ? k_bin<true, true> : k_bin<true, false>;
+    members = bg.G >= kBinMemberBands && (long long)N * bg.cw * bg.gh >= kBinMemberWords * 32;
+  if (members) bg = choose_groups(B, N, nTx, nTy, true);
+  if (bg.NC < 64 || bg.NC % 64 != 0) return hipErrorInvalidValue;  // whole 64-column words
+  const size_t lds = (size_t)bg.cw * bg.gh * (bg.NC / 32) * 4 + (members ? (size_t)bg.NC * 4 : 0);
+  dim3 grid((unsigned)xcd_grid(bg.G, B));
+  const bool cols = bg.ncc > 1;
+  auto k_count = members ? (cols ? k_bin<false, true, true> : k_bin<false, true, false>)
+                         : (cols ? k_bin<false, false, true> : k_bin<false, false, false>);
+  auto k_write = members ? (cols ? k_bin<true, true, true> : k_bin<true, true, false>)
+                         : (cols ? k_bin<true, false, true> : k_bin<true, false, false>);
   PDR_TIMED(PDR_K_BIN_COUNT, st,
             hipLaunchKernelGGL(k_count, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,
-                               gh, G, NC, counts, gtot, (int *)nullptr, (int *)nullptr, cap, hdr));
+                               bg.gh, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr,
+                               (int *)nullptr, cap, hdr));
   PDR_TIMED(PDR_K_BIN_WRITE, st,
             hipLaunchKernelGGL(k_write, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,
-                               gh, G, NC, counts, gtot, tile_off, list, cap, hdr));
+                               bg.gh, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, tile_off, list, cap,
+                               hdr));
   return hipGetLastError();
 }
 

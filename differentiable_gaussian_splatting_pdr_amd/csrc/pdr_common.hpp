@@ -81,16 +81,16 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
   return (__umulhi(n, f.m) + n) >> f.l;
 }
 
-// BR: tile rows of the batch (B * ceil(H / tile)), an upper bound on the
-// binning's row bands.
-inline Layout make_layout(long long BN, long long BT, long long BR, long long cap) {
+// The binning's per-group totals get one slot per tile (a group holds at
+// least one tile).
+inline Layout make_layout(long long BN, long long BT, long long cap) {
   Layout L;
   size_t o = 0;
   L.hdr = o;       o += align256(sizeof(WsHeader));
   L.recs = o;      o += align256(size_t(BN) * sizeof(GRec));
   L.boxes = o;     o += align256(size_t(BN) * 8);
   L.counts = o;    o += align256(size_t(BT) * 4);
-  L.gtot = o;      o += align256(size_t(BR) * 4);
+  L.gtot = o;      o += align256(size_t(BT) * 4);
   L.tile_off = o;  o += align256(size_t(BT + 1) * 4);
   L.list = o;      o += align256(size_t(cap) * 4);
   L.total = o;

@@ -30,6 +30,9 @@ constexpr long long kBinLdsBytes = 60 * 1024 - 512;  // + 4.2 KB of static array
 constexpr int kBinMembers = PDR_BIN_MEMBERS;  // chunks of band members: -1 auto, 0 never, 1 always
 constexpr int kBinMemberBands = 8;            // auto: member lists from this many bands per frame
 constexpr long long kBinMemberWords = 1 << 14;  // ... and this many bit words compacted per group
+constexpr int kBinMinChunkTiles = 4;         // narrowest column chunk of a band
+constexpr long long kBinChunkBelow = 16;      // column chunks when a batch has fewer tile rows
+constexpr long long kBinChunkTarget = 256;    // ... aiming at this many groups
 
 // K1 + count + scan + list write; tile_off/list may be the workspace's own
 // regions or caller buffers (inspection entry point, stamp_valid = false so

@@ -61,8 +61,8 @@ int pdr_splat_tile_size(void);
 
 /* Bytes of workspace for a problem and a (tile, Gaussian) pair capacity.
  * Returns a negative pdr_status on invalid sizes.  The fixed part covers a
- * 256-byte header, 40 bytes per Gaussian, 8 bytes per tile and 4 bytes per
- * tile row (each region rounded up to 256 bytes); every pair takes 4 more
+ * 256-byte header, 40 bytes per Gaussian and 12 bytes per tile (each
+ * region rounded up to 256 bytes); every pair takes 4 more
  * bytes.  max_pairs <= 2^31 - 1. */
 long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long max_pairs);
 

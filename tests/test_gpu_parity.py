@@ -52,10 +52,22 @@ def test_small_parity(orc, case):
 
 
 def test_member_chunks(orc):
-    # a tall ragged frame (10 tile bands) with many Gaussians: binning forms
-    # its chunks from each band's members, several chunks per band
-    B, N, H, W, C = 1, 60000, 150, 420, 1
+    # a ragged frame with many Gaussians (one-row bands cut into column
+    # chunks): binning forms its chunks from each group's members, several
+    # chunks per group
+    B, N, H, W, C = 1, 110000, 150, 420, 1
     p, g = workloads.make_custom(B, N, H, W, C, seed=12, s_range=(0.5, 6.0), mean_margin=4.0)
+    n = check_lists(orc, p, H, W)
+    res = check_against_oracle(orc, p, g, H, W)
+    print("pairs", n, res)
+
+
+@pytest.mark.parametrize("B,N,H,W", [(1, 3000, 64, 1000), (1, 150000, 200, 4096)])
+def test_column_chunks(orc, B, N, H, W):
+    # batches of a few wide frames: binning cuts each one-row band into
+    # column chunks (consecutive chunks of Gaussians for the first shape,
+    # member chunks for the second); ragged last chunk
+    p, g = workloads.make_custom(B, N, H, W, 2, seed=13, s_range=(0.5, 6.0), mean_margin=4.0)
     n = check_lists(orc, p, H, W)
     res = check_against_oracle(orc, p, g, H, W)
     print("pairs", n, res)
