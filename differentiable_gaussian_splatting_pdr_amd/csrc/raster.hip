@@ -462,18 +462,18 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
 // apply the chain rule in place (fp64):
 //   dmu = L^T (S1, S2) with L = [[c/s1, s/s1], [-s/s2, c/s2]],
 //   ds1 = S11/s1, ds2 = S22/s2, dtheta = (s1/s2 - s2/s1) S12, da = A
-// undoing the kappa scale of the whitened coordinates.  A Gaussian whose
-// record has an empty box (culled, or with no pixel in the frame) is in no
-// tile list: its row was zeroed and stays zero, so only its record is read.
+// undoing the kappa scale of the whitened coordinates.  A Gaussian with an
+// empty pixel box (culled, or with no pixel in the frame) is in no tile
+// list: its row was zeroed and stays zero, so only its 8-byte box is read.
 __global__ __launch_bounds__(256) void k_finalize(const float *__restrict__ params,
-                                                  const GRec *__restrict__ recs,
+                                                  const uint2 *__restrict__ boxes,
                                                   float *__restrict__ grad, long long BN, int C,
                                                   const WsHeader *hdr) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= BN) return;
   if (hdr->status & (kStatusOverflow | kStatusStale)) return;
-  const GRec r = recs[i];
-  if ((r.bx & 0xFFFFu) > (r.bx >> 16) || (r.by & 0xFFFFu) > (r.by >> 16)) return;
+  const uint2 bx = boxes[i];
+  if ((bx.x & 0xFFFFu) > (bx.x >> 16) || (bx.y & 0xFFFFu) > (bx.y >> 16)) return;
   const int P = 5 + C;
   const float *g = params + i * P;
   float *o = grad + i * P;
@@ -643,8 +643,8 @@ hipError_t launch_backward(const float *params, const void *grad_image, float *g
   }
   PDR_TIMED(PDR_K_FINALIZE, st,
             hipLaunchKernelGGL(k_finalize, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,
-                               params, (const GRec *)((char *)ws + L.recs), grad_params, BN, C,
-                               (const WsHeader *)hdr));
+                               params, (const uint2 *)((char *)ws + L.boxes), grad_params, BN,
+                               C, (const WsHeader *)hdr));
   return hipGetLastError();
 }
 
