@@ -15,6 +15,7 @@ namespace {
 struct Dims {
   long long BN, BT;
   int nTx, nTy;
+  RowPlan rp;
 };
 
 int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
@@ -29,6 +30,7 @@ int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
   d->BN = BN;
   d->BT = (long long)B * d->nTx * d->nTy;
   if (d->BT + 1 > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
+  d->rp = row_plan(B, N, H, W);
   return PDR_OK;
 }
 
@@ -37,15 +39,20 @@ int validate_radius(float radius) {
 }
 
 // The workspace layout implied by its size: the fixed part, then as many
-// list entries as fit.
+// list entries as fit (4 bytes each; 8 with per-row lists, which take a
+// second list of the same capacity).
 int layout_for(const Dims &d, void *ws, size_t bytes, Layout *L) {
   if (!ws) return PDR_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 255u) != 0) return PDR_ERR_WORKSPACE;
-  Layout fixed = make_layout(d.BN, d.BT, 0);
-  if (bytes < fixed.list) return PDR_ERR_WORKSPACE;
-  long long cap = (long long)((bytes - fixed.list) / 4);
+  Layout fixed = make_layout(d.BN, d.BT, 0, d.rp);
+  if (bytes < fixed.total) return PDR_ERR_WORKSPACE;
+  long long cap = (long long)((bytes - fixed.total) / (d.rp.on ? 8 : 4));
   if (cap > 0x7fffffffLL) cap = 0x7fffffffLL;
-  *L = make_layout(d.BN, d.BT, cap);
+  *L = make_layout(d.BN, d.BT, cap, d.rp);
+  while (d.rp.on && cap > 0 && L->rlist + (size_t)cap * 4 > bytes) {  // alignment padding
+    cap = cap > 64 ? cap - 64 : 0;
+    *L = make_layout(d.BN, d.BT, cap, d.rp);
+  }
   L->total = bytes;
   return PDR_OK;
 }
@@ -145,7 +152,7 @@ long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long
   int rc = validate_sizes(B, N, H, W, C, &d);
   if (rc != PDR_OK) return rc;
   if (max_pairs < 0 || max_pairs > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
-  return (long long)make_layout(d.BN, d.BT, max_pairs).total;
+  return (long long)make_layout(d.BN, d.BT, max_pairs, d.rp).total;
 }
 
 int pdr_splat_forward(const float *params, float *image, int B, int N, int H, int W, int C,

@@ -156,14 +156,18 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
 // total and the overflow flag.  Both passes form the same chunks.
 constexpr int kSegSlots = 4;   // boxes per thread per member-scan segment
 
-template <bool WRITE, bool MEMBERS, bool COLS>
+template <bool WRITE, bool MEMBERS, bool COLS, bool ROWL = false>
 __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ boxes, int B, int N,
                                                      int nTx, int nTy, int gh, int ncc, int cw,
                                                      int G, int NC, int *__restrict__ counts,
                                                      int *__restrict__ gtot,
                                                      int *__restrict__ tile_off,
                                                      int *__restrict__ list, long long cap,
-                                                     WsHeader *hdr) {
+                                                     WsHeader *hdr,
+                                                     const int *__restrict__ rlist = nullptr,
+                                                     const int *__restrict__ fstart = nullptr,
+                                                     long long rcap = 0) {
+  static_assert(!ROWL || MEMBERS, "row lists feed the member scan");
   extern __shared__ unsigned int dyn[];
   __shared__ int base[kMaxGroupTiles];
   __shared__ long long red[kBinThreads / kWave];
@@ -186,6 +190,28 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   unsigned int *bits = dyn;
   int *mem = (int *)(dyn + (size_t)Tg * words);  // MEMBERS only
+
+  // ROWL: the member scan walks the group's tile row's list (gh = 1).  If
+  // the row lists did not fit the workspace (they were not written), it
+  // scans all of the frame's boxes instead: slower, same lists and counts.
+  const int *rl = nullptr;
+  int rn = N;
+  if constexpr (ROWL) {
+    long long part = 0, all = 0;
+    for (int f = tid; f < B; f += kBinThreads) {
+      const long long t = fstart[(size_t)f * (nTy + 1) + nTy];
+      part += f < b ? t : 0;
+      all += t;
+    }
+    const long long fbase = block_sum_ll(part, red);
+    const long long rows_all = block_sum_ll(all, red);
+    // (a frame's row count saturates at 2^31 - 1)
+    if (rows_all <= rcap && rows_all < 0x7fffffffLL) {
+      const int *fs = fstart + (size_t)b * (nTy + 1);
+      rl = rlist + fbase + fs[ty0];
+      rn = fs[ty0 + 1] - fs[ty0];
+    }
+  }
 
   if (WRITE) {
     // base of this group: totals of all groups before it
@@ -311,20 +337,29 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
     };
     const int S = min(NC, kSegSlots * kBinThreads);  // boxes per segment
     uint2 nxt[kSegSlots];
+    int nid[kSegSlots];   // ROWL: the Gaussian indices of the prefetched boxes
     auto load_seg = [&](int s0) {
 #pragma unroll
       for (int k = 0; k < kSegSlots; ++k) {
         const int o = k * kBinThreads + tid;
-        nxt[k] = (o < S && s0 + o < N) ? fb[s0 + o] : make_uint2(kEmptyBox, kEmptyBox);
+        const bool v = o < S && s0 + o < rn;
+        if constexpr (ROWL) {
+          nid[k] = v ? (rl ? rl[s0 + o] : s0 + o) : 0;
+          nxt[k] = v ? fb[nid[k]] : make_uint2(kEmptyBox, kEmptyBox);
+        } else {
+          nxt[k] = v ? fb[s0 + o] : make_uint2(kEmptyBox, kEmptyBox);
+        }
       }
     };
     load_seg(0);
     int cnt = 0;  // members gathered for the current chunk (uniform)
-    for (int s0 = 0; s0 < N; s0 += S) {
+    for (int s0 = 0; s0 < rn; s0 += S) {
       bool in[kSegSlots];
       unsigned long long bal[kSegSlots];
+      int cid[kSegSlots];
 #pragma unroll
       for (int k = 0; k < kSegSlots; ++k) {
+        cid[k] = ROWL ? nid[k] : s0 + k * kBinThreads + tid;
         const uint2 bx = nxt[k];
         const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
         const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
@@ -333,7 +368,7 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
         bal[k] = __builtin_amdgcn_ballot_w64(in[k]);
         if (lane == 0) wcnt[k][wave] = __popcll(bal[k]);
       }
-      if (s0 + S < N) load_seg(s0 + S);
+      if (s0 + S < rn) load_seg(s0 + S);
       __syncthreads();
       // members of this segment, in index order (slot-major, then wave, lane)
       int total = 0, before[kSegSlots];
@@ -354,7 +389,7 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
       const unsigned long long lt_mask = (1ull << lane) - 1ull;
 #pragma unroll
       for (int k = 0; k < kSegSlots; ++k)
-        if (in[k]) mem[cnt + before[k] + __popcll(bal[k] & lt_mask)] = s0 + k * kBinThreads + tid;
+        if (in[k]) mem[cnt + before[k] + __popcll(bal[k] & lt_mask)] = cid[k];
       cnt += total;
       __syncthreads();  // wcnt is rewritten by the next segment
     }
@@ -370,6 +405,157 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
     const long long tot = block_sum_ll(part, red);
     if (tid == 0) gtot[(size_t)b * G + g] = (int)min(tot, 0x7fffffffLL);
   }
+}
+
+// ----------------------------------------------------------------------------
+// Per-row member lists (first level of the two-level binning).
+//
+// k_rows<false>: per (frame, block of RB Gaussians): an LDS bit matrix
+//   [tile row][Gaussian of the block] of box overlaps; the popcount of each
+//   row is stored at rcnt[(frame * nTy + row) * nblk + block].
+// k_rowscan, k_rowstart: rcnt becomes each block's offset within its row's
+//   list, fstart[frame][row] the frame-local start of each row's list and
+//   fstart[frame][nTy] the frame's total.
+// k_rows<true>: the same bit matrix; each row's members are compacted into
+//   rlist at (frames before) + (row start) + rcnt, so every row's list
+//   holds ascending Gaussian indices (blocks in order, bits in order).
+//   Nothing is written if the row pairs of all frames exceed the row list
+//   capacity rcap.
+template <bool WRITE>
+__global__ __launch_bounds__(kBinThreads) void k_rows(const uint2 *__restrict__ boxes, int B,
+                                                      int N, int nTy, int RB, int nblk,
+                                                      int *__restrict__ rcnt,
+                                                      const int *__restrict__ fstart,
+                                                      int *__restrict__ rlist, long long rcap) {
+  extern __shared__ unsigned int rbits[];
+  __shared__ long long red[kBinThreads / kWave];
+  int b, k;
+  if (!xcd_frame_item(blockIdx.x, nblk, B, &b, &k)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int words = RB >> 5;
+  const int j0 = k * RB;
+  const int nj = min(RB, N - j0);
+  long long fbase = 0;
+  if (WRITE) {
+    long long part = 0, all = 0;
+    for (int f = tid; f < B; f += kBinThreads) {
+      const long long t = fstart[(size_t)f * (nTy + 1) + nTy];
+      part += f < b ? t : 0;
+      all += t;
+    }
+    fbase = block_sum_ll(part, red);
+    const long long rows_all = block_sum_ll(all, red);
+    if (rows_all > rcap || rows_all >= 0x7fffffffLL) return;  // uniform: the row lists do not fit
+  }
+  for (int w = tid; w < nTy * words; w += kBinThreads) rbits[w] = 0u;
+  __syncthreads();
+  const uint2 *fb = boxes + (size_t)b * N + j0;
+  for (int jj = tid; jj < nj; jj += kBinThreads) {
+    const uint2 bx = fb[jj];
+    const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
+    const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
+    if (x0 > x1 || y0 > y1) continue;
+    const unsigned int bit = 1u << (jj & 31);
+    for (int r = y0 >> kTileShiftY; r <= (y1 >> kTileShiftY); ++r)
+      atomicOr(&rbits[r * words + (jj >> 5)], bit);
+  }
+  __syncthreads();
+  // a wave per row: rows wave, wave + 8, ...
+  for (int r = wave; r < nTy; r += kBinThreads / kWave) {
+    const size_t ci = ((size_t)b * nTy + r) * nblk + k;
+    const unsigned int *row = rbits + (size_t)r * words;
+    int run = WRITE ? (int)(fbase + fstart[(size_t)b * (nTy + 1) + r] + rcnt[ci]) : 0;
+    for (int seg = 0; seg < words; seg += 2 * kWave) {
+      const int w0 = seg + 2 * lane;  // words even
+      const unsigned long long m =
+          w0 < words ? ((unsigned long long)row[w0] | ((unsigned long long)row[w0 + 1] << 32)) : 0ull;
+      const int c = __popcll(m);
+      const int incl = wave_incl_scan(c);
+      if (WRITE) {
+        int pos = run + incl - c;
+        unsigned long long mm = m;
+        while (mm) {
+          const int q = __ffsll((long long)mm) - 1;
+          rlist[pos++] = j0 + w0 * 32 + q;
+          mm &= mm - 1ull;
+        }
+      }
+      run += wave_read(incl, 63);
+    }
+    if (!WRITE && lane == 0) rcnt[ci] = run;
+  }
+}
+
+// One wave per (frame, tile row): exclusive scan of the row's nblk block
+// counts in place (each lane takes kRowScanPer consecutive counts per
+// round), the row's total into fstart[frame][row].
+constexpr int kRowScanPer = 8;
+__global__ __launch_bounds__(kWave) void k_rowscan(int *__restrict__ rcnt, int B, int nTy, int nblk,
+                                                   int *__restrict__ fstart) {
+  int b, r;
+  if (!xcd_frame_item(blockIdx.x, nTy, B, &b, &r)) return;
+  const int lane = threadIdx.x;
+  int *c = rcnt + ((size_t)b * nTy + r) * nblk;
+  int run = 0;
+  for (int c0 = 0; c0 < nblk; c0 += kWave * kRowScanPer) {
+    const int i0 = c0 + lane * kRowScanPer;
+    int v[kRowScanPer], t = 0;
+#pragma unroll
+    for (int k = 0; k < kRowScanPer; ++k) {
+      v[k] = i0 + k < nblk ? c[i0 + k] : 0;
+      t += v[k];
+    }
+    const int incl = wave_incl_scan(t);
+    int e = run + incl - t;
+#pragma unroll
+    for (int k = 0; k < kRowScanPer; ++k) {
+      if (i0 + k < nblk) c[i0 + k] = e;
+      e += v[k];
+    }
+    run += wave_read(incl, 63);
+  }
+  if (lane == 0) fstart[(size_t)b * (nTy + 1) + r] = run;
+}
+
+// One workgroup per frame: the row totals in fstart[frame][0..nTy) become
+// the rows' list starts (exclusive scan, kRowStartPer rows per thread and
+// round), fstart[frame][nTy] the frame's total, saturated at 2^31 - 1.
+constexpr int kRowStartPer = 4;
+__global__ __launch_bounds__(kBinThreads) void k_rowstart(int nTy, int *__restrict__ fstart) {
+  __shared__ long long wtot[kBinThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int *fs = fstart + (size_t)blockIdx.x * (nTy + 1);
+  long long carry = 0;
+  for (int r0 = 0; r0 < nTy; r0 += kBinThreads * kRowStartPer) {
+    const int i0 = r0 + tid * kRowStartPer;
+    long long v[kRowStartPer], t = 0;
+#pragma unroll
+    for (int k = 0; k < kRowStartPer; ++k) {
+      v[k] = i0 + k < nTy ? fs[i0 + k] : 0;
+      t += v[k];
+    }
+    long long incl = t;  // wave inclusive scan (64-bit, shuffles)
+    for (int d = 1; d < kWave; d <<= 1) {
+      const long long o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    long long wex = 0, tot = 0;
+    for (int w = 0; w < kBinThreads / kWave; ++w) {
+      wex += w < wave ? wtot[w] : 0;
+      tot += wtot[w];
+    }
+    long long e = carry + wex + incl - t;
+#pragma unroll
+    for (int k = 0; k < kRowStartPer; ++k) {
+      if (i0 + k < nTy) fs[i0 + k] = (int)min(e, 0x7fffffffLL);
+      e += v[k];
+    }
+    carry += tot;
+    __syncthreads();  // wtot is rewritten by the next round
+  }
+  if (tid == 0) fs[nTy] = (int)min(carry, 0x7fffffffLL);
 }
 
 // ----------------------------------------------------------------------------
@@ -429,6 +615,61 @@ static BinGroups choose_groups(int B, int N, int nTx, int nTy, bool members) {
   return r;
 }
 
+// Second level of the two-level binning: one tile row per group, cut into
+// column chunks so that the grid has about kBinTargetGroups workgroups (a
+// chunk scans only its row's list, so chunks cost no rescans of the frame).
+static BinGroups row_groups(int B, int N, int nTx, int nTy) {
+  BinGroups r;
+  r.gh = 1;
+  const long long rows_all = (long long)B * nTy;
+  int c = 1;
+  if (rows_all < kBinTargetGroups && nTx >= 2 * kBinMinChunkTiles) {
+    c = (int)((kBinTargetGroups + rows_all - 1) / rows_all);
+    if (c > nTx / kBinMinChunkTiles) c = nTx / kBinMinChunkTiles;
+  }
+  r.cw = (nTx + c - 1) / c;
+  r.ncc = (nTx + r.cw - 1) / r.cw;
+  long long nc = ((long long)N + 63) / 64 * 64;
+  if (nc > kMaxChunk) nc = kMaxChunk;
+  const long long row_max = kBinLdsBytes * 8 / (r.cw + 32) / 64 * 64;
+  if (nc > row_max) nc = row_max;
+  r.NC = (int)nc;
+  r.G = nTy * r.ncc;
+  return r;
+}
+
+// Two-level binning where the one-level member scan would dominate: many
+// Gaussians per frame and a frame cut into many groups, each of which would
+// scan all of the frame's boxes.  The row pass holds a bit matrix of every
+// tile row against RB Gaussians (RB a multiple of 64 between kBinRowBlockMin
+// and kBinRowBlock, smaller when the LDS holds fewer columns).
+RowPlan row_plan(int B, int N, int H, int W) {
+  RowPlan rp;
+  rp.on = false;
+  rp.RB = rp.nblk = 0;
+  rp.B = B;
+  const int nTx = (W + kTileW - 1) / kTileW, nTy = (H + kTileH - 1) / kTileH;
+  rp.nTy = nTy;
+  if (kBinRows == 0) return rp;
+  if (kBinRows < 0) {
+    if (N < kBinRowsMinN) return rp;
+    const BinGroups bg = choose_groups(B, N, nTx, nTy, false);
+    if (!(bg.G >= kBinMemberBands && (long long)N * bg.cw * bg.gh >= kBinMemberWords * 32))
+      return rp;
+  }
+  // blocks small enough for about kBinRowBlocks workgroups over the batch
+  long long rb = (long long)N * B / kBinRowBlocks / 64 * 64;
+  if (rb < kBinRowBlockMin) rb = kBinRowBlockMin;
+  if (rb > kBinRowBlock) rb = kBinRowBlock;
+  const long long rb_lds = kBinLdsBytes * 8 / nTy / 64 * 64;
+  if (rb > rb_lds) rb = rb_lds;
+  if (rb < 64) return rp;
+  rp.RB = (int)rb;
+  rp.nblk = (N + rp.RB - 1) / rp.RB;
+  rp.on = true;
+  return rp;
+}
+
 hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, int C, float radius,
                              void *ws, const Layout &L, bool stamp_valid, hipStream_t st) {
   char *w = (char *)ws;
@@ -455,6 +696,39 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   int nTx = (W + kTileW - 1) / kTileW, nTy = (H + kTileH - 1) / kTileH;
   const hipError_t pe = launch_preprocess(params, B, N, H, W, C, radius, ws, L, stamp_valid, st);
   if (pe != hipSuccess) return pe;
+  const RowPlan rp = row_plan(B, N, H, W);
+  if (rp.on) {
+    // rows: count, scan, write the per-row lists; then each tile row's
+    // tiles from its row's list (member chunks)
+    int *rcnt = (int *)(w + L.rcnt), *fstart = (int *)(w + L.fstart), *rlist = (int *)(w + L.rlist);
+    const BinGroups bg = row_groups(B, N, nTx, nTy);
+    if (bg.NC < 64 || bg.NC % 64 != 0) return hipErrorInvalidValue;
+    const dim3 g1((unsigned)xcd_grid(rp.nblk, B)), g2((unsigned)xcd_grid(bg.G, B));
+    const size_t lds1 = (size_t)nTy * (rp.RB / 32) * 4;
+    const size_t lds2 = (size_t)bg.cw * (bg.NC / 32) * 4 + (size_t)bg.NC * 4;
+    const bool cols = bg.ncc > 1;
+    auto k_rcount = k_rows<false>;
+    auto k_rwrite = k_rows<true>;
+    auto k_count = cols ? k_bin<false, true, true, true> : k_bin<false, true, false, true>;
+    auto k_write = cols ? k_bin<true, true, true, true> : k_bin<true, true, false, true>;
+    PDR_TIMED(PDR_K_BIN_COUNT, st, {
+      hipLaunchKernelGGL(k_rcount, g1, dim3(kBinThreads), lds1, st, boxes, B, N, nTy, rp.RB,
+                         rp.nblk, rcnt, (const int *)fstart, rlist, L.cap);
+      hipLaunchKernelGGL(k_rowscan, dim3((unsigned)xcd_grid(nTy, B)), dim3(kWave), 0, st, rcnt,
+                         B, nTy, rp.nblk, fstart);
+      hipLaunchKernelGGL(k_rowstart, dim3((unsigned)B), dim3(kBinThreads), 0, st, nTy, fstart);
+      hipLaunchKernelGGL(k_rwrite, g1, dim3(kBinThreads), lds1, st, boxes, B, N, nTy, rp.RB,
+                         rp.nblk, rcnt, (const int *)fstart, rlist, L.cap);
+      hipLaunchKernelGGL(k_count, g2, dim3(kBinThreads), lds2, st, boxes, B, N, nTx, nTy, 1,
+                         bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr, (int *)nullptr,
+                         cap, hdr, (const int *)rlist, (const int *)fstart, L.cap);
+    });
+    PDR_TIMED(PDR_K_BIN_WRITE, st,
+              hipLaunchKernelGGL(k_write, g2, dim3(kBinThreads), lds2, st, boxes, B, N, nTx, nTy,
+                                 1, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, tile_off, list, cap,
+                                 hdr, (const int *)rlist, (const int *)fstart, L.cap));
+    return hipGetLastError();
+  }
   BinGroups bg = choose_groups(B, N, nTx, nTy, false);
   // Member lists pay when a frame has many groups (a group meets a small
   // share of its boxes) and the consecutive chunks' compaction is long:
@@ -476,11 +750,12 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   PDR_TIMED(PDR_K_BIN_COUNT, st,
             hipLaunchKernelGGL(k_count, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,
                                bg.gh, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr,
-                               (int *)nullptr, cap, hdr));
+                               (int *)nullptr, cap, hdr, (const int *)nullptr,
+                               (const int *)nullptr, 0LL));
   PDR_TIMED(PDR_K_BIN_WRITE, st,
             hipLaunchKernelGGL(k_write, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,
                                bg.gh, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, tile_off, list, cap,
-                               hdr));
+                               hdr, (const int *)nullptr, (const int *)nullptr, 0LL));
   return hipGetLastError();
 }
 

@@ -55,7 +55,18 @@ constexpr unsigned int kEmptyBox = 0x0000FFFFu;  // x0 = 65535 > x1 = 0
 // Workspace carve-up; every region starts on a 256-byte boundary.
 struct Layout {
   size_t hdr, recs, boxes, counts, gtot, tile_off, list, total;
+  size_t rcnt, fstart, rlist;   // per-row member lists (two-level binning only)
   long long cap;
+};
+
+// Two-level binning plan: per-row member lists built from blocks of RB
+// Gaussians (nblk blocks per frame), then each tile row's tiles from its
+// row's list.  Decided on the host from (B, N, H, W) alone.
+struct RowPlan {
+  bool on;
+  int RB, nblk;
+  long long B;
+  int nTy;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -82,8 +93,10 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
 }
 
 // The binning's per-group totals get one slot per tile (a group holds at
-// least one tile).
-inline Layout make_layout(long long BN, long long BT, long long cap) {
+// least one tile).  With a row plan, the row counts, row starts and row
+// lists follow (the row pairs never exceed the tile pairs, so the list
+// capacity serves both).
+inline Layout make_layout(long long BN, long long BT, long long cap, const RowPlan &rp) {
   Layout L;
   size_t o = 0;
   L.hdr = o;       o += align256(sizeof(WsHeader));
@@ -93,6 +106,12 @@ inline Layout make_layout(long long BN, long long BT, long long cap) {
   L.gtot = o;      o += align256(size_t(BT) * 4);
   L.tile_off = o;  o += align256(size_t(BT + 1) * 4);
   L.list = o;      o += align256(size_t(cap) * 4);
+  L.rcnt = L.fstart = L.rlist = 0;
+  if (rp.on) {
+    L.rcnt = o;    o += align256(size_t(rp.B) * rp.nTy * rp.nblk * 4);
+    L.fstart = o;  o += align256(size_t(rp.B) * (rp.nTy + 1) * 4);
+    L.rlist = o;   o += align256(size_t(cap) * 4);
+  }
   L.total = o;
   L.cap = cap;
   return L;
@@ -203,17 +222,24 @@ __device__ __forceinline__ int value_index(int lane) {
   return idx;
 }
 
-// Blocks of a frame-major grid of (frame, item) are spread so that all items
-// of one frame go to the same XCD (workgroups are dealt to the 8 XCDs round
-// robin), keeping a frame's Gaussian records in one L2.
+// Blocks of a frame-major grid of (frame, item) pairs.  Workgroups are
+// dealt to the 8 XCDs round robin (block i runs on XCD i mod 8), so XCD x
+// is given the x-th eighth of the frame-major pair order: a frame's items
+// share one L2 (or two, at a range boundary) when frames outnumber XCDs,
+// and a frame is spread over several XCDs when they do not.  The grid has
+// 8 * ceil(frames * items / 8) blocks; the excess returns false.
 __device__ __forceinline__ bool xcd_frame_item(int bid, int items, int frames, int *frame, int *item) {
-  int xcd = bid & 7;
-  int local = bid >> 3;
-  *frame = xcd + 8 * (local / items);
-  *item = local % items;
-  return *frame < frames;
+  const unsigned int total = (unsigned int)items * (unsigned int)frames;
+  const unsigned int per = (total + 7u) >> 3;
+  const unsigned int lin = (unsigned int)(bid & 7) * per + ((unsigned int)bid >> 3);
+  if (lin >= total) return false;
+  *frame = (int)(lin / (unsigned int)items);
+  *item = (int)(lin - (unsigned int)*frame * (unsigned int)items);
+  return true;
 }
 
-inline long long xcd_grid(int items, int frames) { return 8LL * ((frames + 7) / 8) * items; }
+inline long long xcd_grid(int items, int frames) {
+  return 8LL * (((long long)items * frames + 7) / 8);
+}
 
 }  // namespace pdr

@@ -33,6 +33,14 @@ constexpr long long kBinMemberWords = 1 << 14;  // ... and this many bit words c
 constexpr int kBinMinChunkTiles = 4;         // narrowest column chunk of a band
 constexpr long long kBinChunkBelow = 16;      // column chunks when a batch has fewer tile rows
 constexpr long long kBinChunkTarget = 256;    // ... aiming at this many groups
+#ifndef PDR_BIN_ROWS
+#define PDR_BIN_ROWS -1
+#endif
+constexpr int kBinRows = PDR_BIN_ROWS;        // two-level binning: -1 auto, 0 never, 1 always
+constexpr int kBinRowsMinN = 16384;           // auto: from this many Gaussians per frame
+constexpr int kBinRowBlock = 4096;            // Gaussians per block of the row pass (at most)
+constexpr int kBinRowBlockMin = 256;          // ... (at least, unless the LDS holds fewer)
+constexpr long long kBinRowBlocks = 1024;     // row-pass workgroups to aim for
 
 // K1 + count + scan + list write; tile_off/list may be the workspace's own
 // regions or caller buffers (inspection entry point, stamp_valid = false so
@@ -40,6 +48,9 @@ constexpr long long kBinChunkTarget = 256;    // ... aiming at this many groups
 hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C, float radius,
                           void *ws, const Layout &L, int *tile_off, int *list, long long cap,
                           bool stamp_valid, hipStream_t st);
+
+// Whether (and how) binning builds per-row member lists first.
+RowPlan row_plan(int B, int N, int H, int W);
 
 // Per-Gaussian records only (the first step of launch_binning).
 hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, int C, float radius,

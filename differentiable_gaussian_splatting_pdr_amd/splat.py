@@ -147,10 +147,12 @@ def bin_lists(params: torch.Tensor, H: int, W: int, radius: float = 3.0):
     dev = params.device
     t = _lib.pdr_splat_tile_size()
     nT = ((H + t - 1) // t) * ((W + t - 1) // t)
-    ws = Workspace(dev, Workspace.bytes_for(B, N, H, W, C, 0))
-    st = _stream(dev)
     cap = _initial_pairs(B, N, H, W)
+    ws = Workspace(dev)
+    st = _stream(dev)
     for _ in range(2):
+        # room for per-row lists too (two-level binning runs faster with them)
+        ws.ensure(Workspace.bytes_for(B, N, H, W, C, cap))
         off = torch.empty(B * nT + 1, dtype=torch.int32, device=dev)
         lst = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
         _lib.pdr_splat_bin(params.data_ptr(), B, N, H, W, C, radius, off.data_ptr(),

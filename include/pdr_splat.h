@@ -63,7 +63,18 @@ int pdr_splat_tile_size(void);
  * Returns a negative pdr_status on invalid sizes.  The fixed part covers a
  * 256-byte header, 40 bytes per Gaussian and 12 bytes per tile (each
  * region rounded up to 256 bytes); every pair takes 4 more
- * bytes.  max_pairs <= 2^31 - 1. */
+ * bytes.  max_pairs <= 2^31 - 1.
+ * Problems with many Gaussians per frame on frames of many tile bands
+ * (N >= 16384 where a frame's bands would each scan all of its boxes) bin
+ * in two levels: first per tile row, then per tile from the row's list.
+ * Their fixed part also holds 4 bytes per (frame, tile row, block of
+ * Gaussians) and 4 per (frame, tile row + 1), and every pair takes 8
+ * bytes (the row lists have the same capacity as the tile lists; a
+ * Gaussian's row pairs never outnumber its tile pairs).  The figure this
+ * function returns covers either case.  Row lists that do not fit (a
+ * workspace sized for fewer pairs, as for counting with pdr_splat_bin) cost
+ * time only: binning then scans every box per group, with the same lists
+ * and pair totals. */
 long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long max_pairs);
 
 /* Forward.  params [B][N][5+C] fp32 -> image [B][H][W][C] fp32 (overwritten).

@@ -198,6 +198,44 @@ def test_overflow_then_regrow(orc):
     check_close(image.cpu().numpy(), ref, np.abs(ref), slk, "image after regrow")
 
 
+def test_two_level_binning_any_workspace(orc):
+    # 65536 Gaussians on a 512 x 512 frame bin in two levels (per tile row,
+    # then per tile from the row's list).  The row lists live in the
+    # workspace: a workspace too small for them still gives the exact pair
+    # total (overflow) and, through pdr_splat_bin, the exact lists.
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import _lib, splat
+    wl, p, g = workloads.make_inputs(4, frames=1)
+    H, W, N, C = wl.H, wl.W, wl.N, wl.C
+    T = _lib.pdr_splat_tile_size()
+    _, off, lst, rect = orc.bin(p, H, W, tile=T)
+    ok = rect[..., 0] >= 0
+    rows = int(np.sum(np.where(ok, rect[..., 3] // T - rect[..., 2] // T + 1, 0)))
+    assert 0 < rows < off[-1]
+    pt = torch.from_numpy(p).cuda()
+    st = torch.cuda.current_stream().cuda_stream
+    nT = ((H + T - 1) // T) * ((W + T - 1) // T)
+    # workspaces for no pairs, for fewer pairs than the row lists, for the rows
+    for pairs in (0, rows - 1, rows):
+        ws = splat.Workspace("cuda:0", splat.Workspace.bytes_for(1, N, H, W, C, pairs))
+        img = torch.empty((1, H, W, C), device="cuda:0")
+        _lib.pdr_splat_forward(pt.data_ptr(), img.data_ptr(), 1, N, H, W, C, 3.0, ws.ptr,
+                               ws.nbytes, st)
+        rc, need = _lib.pdr_splat_check(ws.ptr, st)
+        assert rc == _lib.PDR_ERR_OVERFLOW and need == off[-1], (pairs, rc, need)
+        o = torch.empty(nT + 1, dtype=torch.int32, device="cuda:0")
+        li = torch.empty(int(off[-1]), dtype=torch.int32, device="cuda:0")
+        _lib.pdr_splat_bin(pt.data_ptr(), 1, N, H, W, C, 3.0, o.data_ptr(), li.data_ptr(),
+                           int(off[-1]), ws.ptr, ws.nbytes, st)
+        rc, need = _lib.pdr_splat_check(ws.ptr, st)
+        assert rc == _lib.PDR_OK and need == off[-1], (pairs, rc, need)
+        assert np.array_equal(o.cpu().numpy().astype(np.int64), off), pairs
+        assert np.array_equal(li.cpu().numpy(), lst), pairs
+    image, _ = splat.forward(pt, H, W, 3.0, workspace=ws)
+    ref, slk, _, _ = orc.render(p, H, W)
+    check_close(image.cpu().numpy(), ref, np.abs(ref), slk, "image after regrow")
+
+
 def test_stale_reuse_is_reported():
     import torch
     from differentiable_gaussian_splatting_pdr_amd import _lib, splat
