@@ -194,18 +194,57 @@ __device__ __forceinline__ void tstep(float *v, bool up) {
   }
 }
 
-// Reduce KP per-lane values over the wave.  Afterwards every lane holds the
-// wave total of value index bitrev_log2(KP)(lane & (KP - 1)).
+// One exchange step of the transposed butterfly for MASK in {4, 8}, without
+// selects: the lanes without the MASK bit are whole DPP banks (4-lane groups
+// of a row), so a bank-masked DPP add writes them (own lower-half value plus
+// the partner's) and a second one writes the other banks from the upper
+// half.  The two instructions write every lane of r once.  Inline asm
+// because the compiler forms no DPP add with a partial bank mask.  The
+// hazard recognizer does not look into asm, so each block waits two states
+// (s_nop 1) before its DPP reads, and the MASK 8 blocks, whose results feed
+// the compiler's own DPP steps, also after their write.
+template <int MASK>
+__device__ __forceinline__ float banked_pair_sum(float lo, float hi) {
+  static_assert(MASK == 4 || MASK == 8, "bank-separable lane bits are 2 and 3");
+  float r;
+  if constexpr (MASK == 4) {
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %1, %1 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_shr:4 row_mask:0xf bank_mask:0xa"
+        : "=&v"(r)
+        : "v"(lo), "v"(hi));
+  } else {
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %1, %1 row_shl:8 row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_shr:8 row_mask:0xf bank_mask:0xc\n\t"
+        "s_nop 1"
+        : "=&v"(r)
+        : "v"(lo), "v"(hi));
+  }
+  return r;
+}
+
+template <int HALF, int MASK>
+__device__ __forceinline__ void bstep(float *v) {
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) v[i] = banked_pair_sum<MASK>(v[i], v[i + HALF]);
+}
+
+// Reduce KP per-lane values over the wave.  Transposed steps over the lane
+// bits 2, 3 (bank-masked DPP), then 0, 1 (quad_perm DPP with selects) and,
+// for KP = 32, 4 (ds_swizzle); the remaining bits are all-reduce steps.
+// Afterwards every lane holds the wave total of value value_index<KP>(lane);
+// the lanes with reduce_issuer<KP>(lane) hold each value once.
 template <int KP>
 __device__ __forceinline__ float wave_reduce_transposed(float *v, int lane) {
   static_assert(KP == 8 || KP == 16 || KP == 32, "KP");
-  tstep<KP / 2, 1>(v, lane & 1);
-  tstep<KP / 4, 2>(v, lane & 2);
-  tstep<KP / 8, 4>(v, lane & 4);
-  if constexpr (KP >= 16) tstep<KP / 16, 8>(v, lane & 8);
-  if constexpr (KP >= 32) tstep<KP / 32, 16>(v, lane & 16);
+  bstep<KP / 2, 4>(v);
+  bstep<KP / 4, 8>(v);
+  tstep<KP / 8, 1>(v, lane & 1);
+  if constexpr (KP >= 16) tstep<KP / 16, 2>(v, lane & 2);
+  if constexpr (KP >= 32) tstep<1, 16>(v, lane & 16);
   float r = v[0];
-  if constexpr (KP < 16) r = xor_sum<8>(r);
+  if constexpr (KP < 16) r = xor_sum<2>(r);
   // the last exchanges through the LDS crossbar (no VALU but the add;
   // measured faster than the permlane swaps): ds_swizzle for lane ^ 16,
   // ds_bpermute for lane ^ 32
@@ -215,11 +254,17 @@ __device__ __forceinline__ float wave_reduce_transposed(float *v, int lane) {
 
 template <int KP>
 __device__ __forceinline__ int value_index(int lane) {
-  int idx = 0;
-#pragma unroll
-  for (int s = 0, h = KP / 2; h >= 1; ++s, h >>= 1)
-    if (lane & (1 << s)) idx += h;
+  int idx = ((lane & 4) ? KP / 2 : 0) + ((lane & 8) ? KP / 4 : 0) + ((lane & 1) ? KP / 8 : 0);
+  if constexpr (KP >= 16) idx += (lane & 2) ? KP / 16 : 0;
+  if constexpr (KP >= 32) idx += (lane & 16) ? 1 : 0;
   return idx;
+}
+
+// The KP lanes (one per value) whose all-reduce lane bits are zero.
+template <int KP>
+__device__ __forceinline__ bool reduce_issuer(int lane) {
+  constexpr int kAll = KP == 8 ? (2 | 16 | 32) : (KP == 16 ? (16 | 32) : 32);
+  return (lane & kAll) == 0;
 }
 
 // Blocks of a frame-major grid of (frame, item) pairs.  Workgroups are

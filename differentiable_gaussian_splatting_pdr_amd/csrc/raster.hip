@@ -380,9 +380,9 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
   constexpr bool kXpose = UseXpose<CP>::value;
   __shared__ __align__(16) float red_all[kXpose ? WL::kWaves * KP * kRedRow : 1];
   float *red = red_all + (kXpose ? wave * KP * kRedRow : 0);  // this wave's rows
-  const int vidx = kXpose ? lane / (kWave / KP) : value_index<KP>(lane & (KP - 1));
+  const int vidx = kXpose ? lane / (kWave / KP) : value_index<KP>(lane);
   int slot = -1;
-  if (kXpose ? lane % (kWave / KP) == 0 : lane < KP) {
+  if (kXpose ? lane % (kWave / KP) == 0 : reduce_issuer<KP>(lane)) {
     if (vidx < CP) slot = vidx < cc ? 5 + c0 + vidx : -1;
     else if (vidx < K) slot = vidx - CP;
   }

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
   const float thr_span = thr * (1.0f + kSpanMargin);
   int *st_start = s_start[wv], *st_xs = s_xs[wv], *st_row = s_row[wv];
   float *st_sum = s_sum[wv];
-  const int vidx = value_index<KP>(lane & (KP - 1));
+  const int vidx = value_index<KP>(lane);
 
   for (int j = 0; j < kSpanPerWave; ++j) {
     const int n = item * kSpanPerBlock + j * kSpanWaves + wv;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
       }
     }
     const float tot = wave_reduce_transposed<KP>(part, lane);
-    if (lane < KP) st_sum[vidx] = tot;
+    if (reduce_issuer<KP>(lane)) st_sum[vidx] = tot;
     // the chain rule (fp64), undoing the kappa scale of the whitened rows:
     //   dmu = L^T (S1, S2), ds1 = S11 / s1, ds2 = S22 / s2,
     //   dtheta = (s1/s2 - s2/s1) S12, da = A
