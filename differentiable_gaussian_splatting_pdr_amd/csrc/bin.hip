@@ -335,65 +335,76 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
       compact((cnt + 31) >> 5, [&](int j) { return mem[j]; });
       __syncthreads();  // the member list is refilled next
     };
-    const int S = min(NC, kSegSlots * kBinThreads);  // boxes per segment
-    uint2 nxt[kSegSlots];
-    int nid[kSegSlots];   // ROWL: the Gaussian indices of the prefetched boxes
-    auto load_seg = [&](int s0) {
-#pragma unroll
-      for (int k = 0; k < kSegSlots; ++k) {
-        const int o = k * kBinThreads + tid;
-        const bool v = o < S && s0 + o < rn;
-        if constexpr (ROWL) {
-          nid[k] = v ? (rl ? rl[s0 + o] : s0 + o) : 0;
-          nxt[k] = v ? fb[nid[k]] : make_uint2(kEmptyBox, kEmptyBox);
-        } else {
-          nxt[k] = v ? fb[s0 + o] : make_uint2(kEmptyBox, kEmptyBox);
-        }
-      }
-    };
-    load_seg(0);
-    int cnt = 0;  // members gathered for the current chunk (uniform)
-    for (int s0 = 0; s0 < rn; s0 += S) {
-      bool in[kSegSlots];
-      unsigned long long bal[kSegSlots];
-      int cid[kSegSlots];
-#pragma unroll
-      for (int k = 0; k < kSegSlots; ++k) {
-        cid[k] = ROWL ? nid[k] : s0 + k * kBinThreads + tid;
-        const uint2 bx = nxt[k];
-        const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
-        const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
-        in[k] = x0 <= x1 && (y0 >> kTileShiftY) < ty0 + ah && (y1 >> kTileShiftY) >= ty0 &&
-                (!COLS || ((x0 >> kTileShiftX) < cx0 + aw && (x1 >> kTileShiftX) >= cx0));
-        bal[k] = __builtin_amdgcn_ballot_w64(in[k]);
-        if (lane == 0) wcnt[k][wave] = __popcll(bal[k]);
-      }
-      if (s0 + S < rn) load_seg(s0 + S);
-      __syncthreads();
-      // members of this segment, in index order (slot-major, then wave, lane)
-      int total = 0, before[kSegSlots];
-#pragma unroll
-      for (int k = 0; k < kSegSlots; ++k) {
-        int wsum = 0, wpre = 0;
-        for (int w = 0; w < kBinThreads / kWave; ++w) {
-          wpre += w < wave ? wcnt[k][w] : 0;
-          wsum += wcnt[k][w];
-        }
-        before[k] = total + wpre;
-        total += wsum;
-      }
-      if (cnt + total > NC) {  // total <= S <= NC
+    bool direct = false;
+    if constexpr (ROWL && !COLS) direct = rl != nullptr;
+    if (direct) {
+      // a whole tile row: every entry of the row's list meets the group
+      for (int c0 = 0; c0 < rn; c0 += NC) {
+        const int cnt = min(NC, rn - c0);
+        for (int j = tid; j < cnt; j += kBinThreads) mem[j] = rl[c0 + j];
         flush(cnt);
-        cnt = 0;
       }
-      const unsigned long long lt_mask = (1ull << lane) - 1ull;
-#pragma unroll
-      for (int k = 0; k < kSegSlots; ++k)
-        if (in[k]) mem[cnt + before[k] + __popcll(bal[k] & lt_mask)] = cid[k];
-      cnt += total;
-      __syncthreads();  // wcnt is rewritten by the next segment
+    } else {
+      const int S = min(NC, kSegSlots * kBinThreads);  // boxes per segment
+      uint2 nxt[kSegSlots];
+      int nid[kSegSlots];   // ROWL: the Gaussian indices of the prefetched boxes
+      auto load_seg = [&](int s0) {
+  #pragma unroll
+        for (int k = 0; k < kSegSlots; ++k) {
+          const int o = k * kBinThreads + tid;
+          const bool v = o < S && s0 + o < rn;
+          if constexpr (ROWL) {
+            nid[k] = v ? (rl ? rl[s0 + o] : s0 + o) : 0;
+            nxt[k] = v ? fb[nid[k]] : make_uint2(kEmptyBox, kEmptyBox);
+          } else {
+            nxt[k] = v ? fb[s0 + o] : make_uint2(kEmptyBox, kEmptyBox);
+          }
+        }
+      };
+      load_seg(0);
+      int cnt = 0;  // members gathered for the current chunk (uniform)
+      for (int s0 = 0; s0 < rn; s0 += S) {
+        bool in[kSegSlots];
+        unsigned long long bal[kSegSlots];
+        int cid[kSegSlots];
+  #pragma unroll
+        for (int k = 0; k < kSegSlots; ++k) {
+          cid[k] = ROWL ? nid[k] : s0 + k * kBinThreads + tid;
+          const uint2 bx = nxt[k];
+          const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
+          const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
+          in[k] = x0 <= x1 && (y0 >> kTileShiftY) < ty0 + ah && (y1 >> kTileShiftY) >= ty0 &&
+                  (!COLS || ((x0 >> kTileShiftX) < cx0 + aw && (x1 >> kTileShiftX) >= cx0));
+          bal[k] = __builtin_amdgcn_ballot_w64(in[k]);
+          if (lane == 0) wcnt[k][wave] = __popcll(bal[k]);
+        }
+        if (s0 + S < rn) load_seg(s0 + S);
+        __syncthreads();
+        // members of this segment, in index order (slot-major, then wave, lane)
+        int total = 0, before[kSegSlots];
+  #pragma unroll
+        for (int k = 0; k < kSegSlots; ++k) {
+          int wsum = 0, wpre = 0;
+          for (int w = 0; w < kBinThreads / kWave; ++w) {
+            wpre += w < wave ? wcnt[k][w] : 0;
+            wsum += wcnt[k][w];
+          }
+          before[k] = total + wpre;
+          total += wsum;
+        }
+        if (cnt + total > NC) {  // total <= S <= NC
+          flush(cnt);
+          cnt = 0;
+        }
+        const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  #pragma unroll
+        for (int k = 0; k < kSegSlots; ++k)
+          if (in[k]) mem[cnt + before[k] + __popcll(bal[k] & lt_mask)] = cid[k];
+        cnt += total;
+        __syncthreads();  // wcnt is rewritten by the next segment
+      }
+      if (cnt > 0) flush(cnt);
     }
-    if (cnt > 0) flush(cnt);
   }
   __syncthreads();
   if (!WRITE) {
