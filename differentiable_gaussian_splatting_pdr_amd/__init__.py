@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     PdrError,
     pdr_splat_backward,
     pdr_splat_bin,
+    pdr_splat_bin_variant,
     pdr_splat_check,
     pdr_splat_forward,
     pdr_splat_tile_size,
@@ -21,6 +22,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "LIB_PATH", "PdrError", "pdr_splat_backward", "pdr_splat_bin", "pdr_splat_check",
+    "LIB_PATH", "PdrError", "pdr_splat_backward", "pdr_splat_bin", "pdr_splat_bin_variant",
+    "pdr_splat_check",
     "pdr_splat_forward", "pdr_splat_tile_size", "pdr_splat_workspace_bytes", "status_string",
 ]

@@ -22,6 +22,7 @@ PDR_ERR_STALE = -5
 
 EXPORTED = (
     "pdr_splat_tile_size",
+    "pdr_splat_bin_variant",
     "pdr_splat_workspace_bytes",
     "pdr_splat_forward",
     "pdr_splat_backward",
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
         i, ll, f, vp, sz = ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
         L.pdr_splat_tile_size.argtypes = []
         L.pdr_splat_tile_size.restype = i
+        L.pdr_splat_bin_variant.argtypes = [i, i, i, i]
+        L.pdr_splat_bin_variant.restype = i
         L.pdr_splat_workspace_bytes.argtypes = [i, i, i, i, i, ll]
         L.pdr_splat_workspace_bytes.restype = ll
         L.pdr_splat_forward.argtypes = [vp, vp, i, i, i, i, i, f, vp, sz, vp]
@@ -121,6 +124,14 @@ def status_string(status: int) -> str:
 
 def pdr_splat_tile_size() -> int:
     return lib().pdr_splat_tile_size()
+
+
+PDR_BIN_MEMBERS, PDR_BIN_COLUMNS, PDR_BIN_TWO_LEVEL = 1, 2, 4
+
+
+def pdr_splat_bin_variant(B, N, H, W) -> int:
+    """Bit set of PDR_BIN_* for the binning a problem of this size takes."""
+    return _raise(lib().pdr_splat_bin_variant(B, N, H, W), "pdr_splat_bin_variant")
 
 
 def pdr_splat_workspace_bytes(B, N, H, W, C, max_pairs) -> int:

@@ -147,6 +147,12 @@ extern "C" {
 
 int pdr_splat_tile_size(void) { return kTileW; }
 
+int pdr_splat_bin_variant(int B, int N, int H, int W) {
+  Dims d;
+  const int rc = validate_sizes(B, N, H, W, 1, &d);
+  return rc != PDR_OK ? rc : bin_variant(B, N, H, W);
+}
+
 long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long max_pairs) {
   Dims d;
   int rc = validate_sizes(B, N, H, W, C, &d);

@@ -626,6 +626,15 @@ static BinGroups choose_groups(int B, int N, int nTx, int nTy, bool members) {
   return r;
 }
 
+// Member lists pay when a frame has many groups (a group meets a small
+// share of its boxes) and the consecutive chunks' compaction is long:
+// every group compacts N * Tg / 32 bit words, which the member lists cut
+// to the group's share.  Measured on MI355X: 26% faster binning at 16
+// bands and N * Tg = 2^22, a tie at 32 bands and 2^18, slower below.
+static bool member_rule(int N, const BinGroups &bg) {
+  return bg.G >= kBinMemberBands && (long long)N * bg.cw * bg.gh >= kBinMemberWords * 32;
+}
+
 // Second level of the two-level binning: one tile row per group, cut into
 // column chunks so that the grid has about kBinTargetGroups workgroups (a
 // chunk scans only its row's list, so chunks cost no rescans of the frame).
@@ -664,9 +673,7 @@ RowPlan row_plan(int B, int N, int H, int W) {
   if (kBinRows == 0) return rp;
   if (kBinRows < 0) {
     if (N < kBinRowsMinN) return rp;
-    const BinGroups bg = choose_groups(B, N, nTx, nTy, false);
-    if (!(bg.G >= kBinMemberBands && (long long)N * bg.cw * bg.gh >= kBinMemberWords * 32))
-      return rp;
+    if (!member_rule(N, choose_groups(B, N, nTx, nTy, false))) return rp;
   }
   // blocks small enough for about kBinRowBlocks workgroups over the batch
   long long rb = (long long)N * B / kBinRowBlocks / 64 * 64;
@@ -679,6 +686,33 @@ RowPlan row_plan(int B, int N, int H, int W) {
   rp.nblk = (N + rp.RB - 1) / rp.RB;
   rp.on = true;
   return rp;
+}
+
+// The binning variant of a problem, decided from (B, N, H, W) alone.
+struct BinPlan {
+  RowPlan rp;     // two-level when rp.on
+  BinGroups bg;   // the (second-level) groups
+  bool members;   // member chunks (always with rp.on)
+};
+
+static BinPlan plan_binning(int B, int N, int H, int W) {
+  BinPlan p;
+  const int nTx = (W + kTileW - 1) / kTileW, nTy = (H + kTileH - 1) / kTileH;
+  p.rp = row_plan(B, N, H, W);
+  if (p.rp.on) {
+    p.bg = row_groups(B, N, nTx, nTy);
+    p.members = true;
+    return p;
+  }
+  p.bg = choose_groups(B, N, nTx, nTy, false);
+  p.members = kBinMembers > 0 || (kBinMembers < 0 && member_rule(N, p.bg));
+  if (p.members) p.bg = choose_groups(B, N, nTx, nTy, true);
+  return p;
+}
+
+int bin_variant(int B, int N, int H, int W) {
+  const BinPlan p = plan_binning(B, N, H, W);
+  return (p.members ? 1 : 0) | (p.bg.ncc > 1 ? 2 : 0) | (p.rp.on ? 4 : 0);
 }
 
 hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, int C, float radius,
@@ -707,12 +741,13 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   int nTx = (W + kTileW - 1) / kTileW, nTy = (H + kTileH - 1) / kTileH;
   const hipError_t pe = launch_preprocess(params, B, N, H, W, C, radius, ws, L, stamp_valid, st);
   if (pe != hipSuccess) return pe;
-  const RowPlan rp = row_plan(B, N, H, W);
+  const BinPlan plan = plan_binning(B, N, H, W);
+  const RowPlan &rp = plan.rp;
   if (rp.on) {
     // rows: count, scan, write the per-row lists; then each tile row's
     // tiles from its row's list (member chunks)
     int *rcnt = (int *)(w + L.rcnt), *fstart = (int *)(w + L.fstart), *rlist = (int *)(w + L.rlist);
-    const BinGroups bg = row_groups(B, N, nTx, nTy);
+    const BinGroups &bg = plan.bg;
     if (bg.NC < 64 || bg.NC % 64 != 0) return hipErrorInvalidValue;
     const dim3 g1((unsigned)xcd_grid(rp.nblk, B)), g2((unsigned)xcd_grid(bg.G, B));
     const size_t lds1 = (size_t)nTy * (rp.RB / 32) * 4;
@@ -740,16 +775,8 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
                                  hdr, (const int *)rlist, (const int *)fstart, L.cap));
     return hipGetLastError();
   }
-  BinGroups bg = choose_groups(B, N, nTx, nTy, false);
-  // Member lists pay when a frame has many groups (a group meets a small
-  // share of its boxes) and the consecutive chunks' compaction is long:
-  // every group compacts N * Tg / 32 bit words, which the member lists cut
-  // to the group's share.  Measured on MI355X: 26% faster binning at 16
-  // bands and N * Tg = 2^22, a tie at 32 bands and 2^18, slower below.
-  bool members = kBinMembers > 0;
-  if (kBinMembers < 0)
-    members = bg.G >= kBinMemberBands && (long long)N * bg.cw * bg.gh >= kBinMemberWords * 32;
-  if (members) bg = choose_groups(B, N, nTx, nTy, true);
+  const BinGroups &bg = plan.bg;
+  const bool members = plan.members;
   if (bg.NC < 64 || bg.NC % 64 != 0) return hipErrorInvalidValue;  // whole 64-column words
   const size_t lds = (size_t)bg.cw * bg.gh * (bg.NC / 32) * 4 + (members ? (size_t)bg.NC * 4 : 0);
   dim3 grid((unsigned)xcd_grid(bg.G, B));

@@ -51,6 +51,8 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
 
 // Whether (and how) binning builds per-row member lists first.
 RowPlan row_plan(int B, int N, int H, int W);
+// bit 0: member chunks, bit 1: column chunks, bit 2: two-level (row lists)
+int bin_variant(int B, int N, int H, int W);
 
 // Per-Gaussian records only (the first step of launch_binning).
 hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, int C, float radius,

@@ -59,6 +59,16 @@ enum pdr_status {
 /* Tile edge in pixels used by binning and raster (16). */
 int pdr_splat_tile_size(void);
 
+/* Inspection: which binning variant a problem of this size takes (host
+ * only, no device call).  A bit set of PDR_BIN_MEMBERS (chunks are formed
+ * from the Gaussians whose pixel box meets a group's tiles, instead of
+ * consecutive Gaussians), PDR_BIN_COLUMNS (tile rows cut into column
+ * chunks) and PDR_BIN_TWO_LEVEL (per-tile-row member lists first); 0 is
+ * consecutive chunks over bands of whole tile rows.  Every variant yields
+ * the same lists.  Negative pdr_status on invalid sizes. */
+enum { PDR_BIN_MEMBERS = 1, PDR_BIN_COLUMNS = 2, PDR_BIN_TWO_LEVEL = 4 };
+int pdr_splat_bin_variant(int B, int N, int H, int W);
+
 /* Bytes of workspace for a problem and a (tile, Gaussian) pair capacity.
  * Returns a negative pdr_status on invalid sizes.  The fixed part covers a
  * 256-byte header, 40 bytes per Gaussian and 12 bytes per tile (each

@@ -175,3 +175,31 @@ def test_concat_entry_points_validate():
                                        0, None) == -1
     assert L.pdr_splat_backward_concat(FAKE, FAKE, 2, FAKE, None, 1, 4, 8, 8, 1, 3.0, ws + 8,
                                        1 << 20, 0, None) == -2
+
+
+# The binning variant rule (host logic): bit 0 member chunks, bit 1 column
+# chunks, bit 2 two-level.  Column chunks only when the whole batch has
+# fewer than 16 tile rows; member chunks when a frame has at least 8 groups
+# and a group would compact at least 2^19 bit words; two-level when that
+# member rule holds with N >= 16384.
+@pytest.mark.parametrize("shape,variant", [
+    ((1, 256, 64, 64), 0), ((160, 1024, 64, 64), 0), ((384, 4096, 128, 128), 0),
+    ((192, 8192, 128, 256), 0),            # the batched workloads: consecutive chunks
+    ((80, 65536, 512, 512), 5),            # 2560 tile rows: a group per row, no column chunks
+    ((1, 12000, 256, 1024), 1),            # 16 rows of 64 tiles: 12000 * 64 >= 2^19
+    ((1, 16383, 512, 512), 0),             # 32 rows of 32 tiles: 16383 * 32 < 2^19
+    ((1, 16384, 512, 512), 7),             # ... 16384 * 32 = 2^19 and N >= 16384
+    ((1, 3000, 64, 1000), 2), ((1, 20000, 20, 16384), 2),
+    ((1, 16000, 240, 10240), 3),           # 15 rows cut into 36-tile chunks
+    ((1, 262144, 2048, 2048), 7), ((4, 65536, 1024, 1024), 7),
+])
+def test_bin_variant_rule(shape, variant):
+    assert _lib.lib().pdr_splat_bin_variant(*shape) == variant
+
+
+def test_bin_variant_validates():
+    L = _lib.lib()
+    assert L.pdr_splat_bin_variant(0, 10, 16, 16) == _lib.PDR_ERR_INVALID_ARG
+    assert L.pdr_splat_bin_variant(1, 10, 40000, 16) == _lib.PDR_ERR_INVALID_ARG
+    with pytest.raises(_lib.PdrError):
+        _lib.pdr_splat_bin_variant(1, 0, 16, 16)

@@ -51,26 +51,30 @@ def test_small_parity(orc, case):
     print(case, res)
 
 
-def test_member_chunks(orc):
-    # a ragged frame with many Gaussians (one-row bands cut into column
-    # chunks): binning forms its chunks from each group's members, several
-    # chunks per group
-    B, N, H, W, C = 1, 110000, 150, 420, 1
-    p, g = workloads.make_custom(B, N, H, W, C, seed=12, s_range=(0.5, 6.0), mean_margin=4.0)
-    n = check_lists(orc, p, H, W)
-    res = check_against_oracle(orc, p, g, H, W)
-    print("pairs", n, res)
+# Every binning variant (pdr_splat_bin_variant: bit 0 member chunks, bit 1
+# column chunks, bit 2 two-level) must yield the oracle's lists; each shape
+# asserts the variant it is there to cover.
+BIN_VARIANTS = [
+    # (B, N, H, W), variant
+    ((2, 300, 64, 64), 0),          # consecutive chunks over bands of whole tile rows
+    ((1, 12000, 256, 1024), 1),     # member chunks, 16 one-row bands of 64 tiles
+    ((1, 3000, 64, 1000), 2),       # consecutive chunks, one-row bands cut into column chunks
+    ((1, 16000, 240, 10240), 3),    # member chunks over column chunks
+    ((1, 110000, 150, 420), 7),     # two-level, a ragged frame
+    ((1, 150000, 200, 4096), 7),    # two-level, a wide frame
+]
 
 
-@pytest.mark.parametrize("B,N,H,W", [(1, 3000, 64, 1000), (1, 150000, 200, 4096)])
-def test_column_chunks(orc, B, N, H, W):
-    # batches of a few wide frames: binning cuts each one-row band into
-    # column chunks (consecutive chunks of Gaussians for the first shape,
-    # member chunks for the second); ragged last chunk
+@pytest.mark.parametrize("shape,variant", BIN_VARIANTS,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else "v%d" % v)
+def test_binning_variants(orc, shape, variant):
+    from differentiable_gaussian_splatting_pdr_amd import _lib
+    B, N, H, W = shape
+    assert _lib.pdr_splat_bin_variant(B, N, H, W) == variant
     p, g = workloads.make_custom(B, N, H, W, 2, seed=13, s_range=(0.5, 6.0), mean_margin=4.0)
     n = check_lists(orc, p, H, W)
     res = check_against_oracle(orc, p, g, H, W)
-    print("pairs", n, res)
+    print(shape, "variant", variant, "pairs", n, res)
 
 
 @pytest.mark.parametrize("radius", [1.0, 2.0, 4.5, 12.0])
@@ -198,15 +202,19 @@ def test_overflow_then_regrow(orc):
     check_close(image.cpu().numpy(), ref, np.abs(ref), slk, "image after regrow")
 
 
-def test_two_level_binning_any_workspace(orc):
-    # 65536 Gaussians on a 512 x 512 frame bin in two levels (per tile row,
-    # then per tile from the row's list).  The row lists live in the
-    # workspace: a workspace too small for them still gives the exact pair
-    # total (overflow) and, through pdr_splat_bin, the exact lists.
+@pytest.mark.parametrize("frames,variant", [(1, 7), (64, 5)])
+def test_two_level_binning_any_workspace(orc, frames, variant):
+    # 65536 Gaussians per 512 x 512 frame bin in two levels (per tile row,
+    # then per tile from the row's list; with one frame the rows are cut
+    # into column chunks, with 64 frames a group holds a whole row).  The
+    # row lists live in the workspace: a workspace too small for them still
+    # gives the exact pair total (overflow) and, through pdr_splat_bin, the
+    # exact lists.
     import torch
     from differentiable_gaussian_splatting_pdr_amd import _lib, splat
-    wl, p, g = workloads.make_inputs(4, frames=1)
-    H, W, N, C = wl.H, wl.W, wl.N, wl.C
+    wl, p, g = workloads.make_inputs(4, frames=frames)
+    B, H, W, N, C = frames, wl.H, wl.W, wl.N, wl.C
+    assert _lib.pdr_splat_bin_variant(B, N, H, W) == variant
     T = _lib.pdr_splat_tile_size()
     _, off, lst, rect = orc.bin(p, H, W, tile=T)
     ok = rect[..., 0] >= 0
@@ -217,23 +225,24 @@ def test_two_level_binning_any_workspace(orc):
     nT = ((H + T - 1) // T) * ((W + T - 1) // T)
     # workspaces for no pairs, for fewer pairs than the row lists, for the rows
     for pairs in (0, rows - 1, rows):
-        ws = splat.Workspace("cuda:0", splat.Workspace.bytes_for(1, N, H, W, C, pairs))
-        img = torch.empty((1, H, W, C), device="cuda:0")
-        _lib.pdr_splat_forward(pt.data_ptr(), img.data_ptr(), 1, N, H, W, C, 3.0, ws.ptr,
+        ws = splat.Workspace("cuda:0", splat.Workspace.bytes_for(B, N, H, W, C, pairs))
+        img = torch.empty((B, H, W, C), device="cuda:0")
+        _lib.pdr_splat_forward(pt.data_ptr(), img.data_ptr(), B, N, H, W, C, 3.0, ws.ptr,
                                ws.nbytes, st)
         rc, need = _lib.pdr_splat_check(ws.ptr, st)
         assert rc == _lib.PDR_ERR_OVERFLOW and need == off[-1], (pairs, rc, need)
-        o = torch.empty(nT + 1, dtype=torch.int32, device="cuda:0")
+        o = torch.empty(B * nT + 1, dtype=torch.int32, device="cuda:0")
         li = torch.empty(int(off[-1]), dtype=torch.int32, device="cuda:0")
-        _lib.pdr_splat_bin(pt.data_ptr(), 1, N, H, W, C, 3.0, o.data_ptr(), li.data_ptr(),
+        _lib.pdr_splat_bin(pt.data_ptr(), B, N, H, W, C, 3.0, o.data_ptr(), li.data_ptr(),
                            int(off[-1]), ws.ptr, ws.nbytes, st)
         rc, need = _lib.pdr_splat_check(ws.ptr, st)
         assert rc == _lib.PDR_OK and need == off[-1], (pairs, rc, need)
         assert np.array_equal(o.cpu().numpy().astype(np.int64), off), pairs
         assert np.array_equal(li.cpu().numpy(), lst), pairs
-    image, _ = splat.forward(pt, H, W, 3.0, workspace=ws)
-    ref, slk, _, _ = orc.render(p, H, W)
-    check_close(image.cpu().numpy(), ref, np.abs(ref), slk, "image after regrow")
+        del ws, img, o, li
+    image, _ = splat.forward(pt, H, W, 3.0)
+    ref, slk, _, _ = orc.render(p[:1], H, W)
+    check_close(image[:1].cpu().numpy(), ref, np.abs(ref), slk, "first frame after regrow")
 
 
 def test_stale_reuse_is_reported():
