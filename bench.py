@@ -9,7 +9,10 @@ N(0, 0.5), 3-sigma truncation), seeded synthetic inputs resident in HBM.
 
 Prints one JSON line.  ``value`` is Gaussian-pixel evaluations per second for
 forward + backward: the number of (Gaussian, pixel) pairs inside the
-truncation, counted exactly by the CPU oracle, divided by the step time.
+truncation -- counted on the GPU by the library's support count, which walks
+the forward raster's lists in the same fp32 arithmetic, outside the timed
+region -- divided by the step time.  The CPU leg reports the fp64 oracle's
+count of the same pairs beside it.
 """
 from __future__ import annotations
 
@@ -162,7 +165,8 @@ def source_digest(files):
 
 def cpu_baseline_leg(params, grad, wl, radius, budget_s, want_count=True):
     """The oracle (fp64 CPU) timed on this host's cores on a bounded sample of
-    the workload's frames; also counts the support pairs of the full batch."""
+    the workload's frames; also counts the support pairs of the full batch
+    (a cross-check of the GPU's count)."""
     import numpy as np
     import oracle
     oracle.build(force=False)
@@ -249,6 +253,15 @@ def main():
     del probe, off, lst
     ws_bytes = _lib.pdr_splat_workspace_bytes(B, N, H, W, C, tile_pairs)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    # the work count: (Gaussian, pixel) pairs inside the truncation, on the GPU
+    count = torch.zeros(1, dtype=torch.int64, device=dev)
+    _lib.pdr_splat_count_support(params.data_ptr(), B, N, H, W, C, args.radius,
+                                 count.data_ptr(), ws.data_ptr(), ws_bytes, st)
+    rc, _ = _lib.pdr_splat_check(ws.data_ptr(), st)
+    if rc != 0:
+        raise SystemExit("support count failed: %s" % _lib.status_string(rc))
+    support_pairs = int(count.item())
 
     def step():
         _lib.pdr_splat_forward(params.data_ptr(), image.data_ptr(), B, N, H, W, C, args.radius,
@@ -362,9 +375,13 @@ def main():
     algo_out = backward_algo_leg(args, _lib, torch, B, N, H, W, C, params, grad_image, grad_params,
                                  ws, ws_bytes, st)
 
-    cpu, support_pairs = None, None
+    cpu = None
     if not args.no_cpu_baseline:
-        cpu, support_pairs = cpu_baseline_leg(params_np, grad_np, wl, args.radius, args.cpu_budget)
+        cpu, oracle_pairs = cpu_baseline_leg(params_np, grad_np, wl, args.radius, args.cpu_budget)
+        # cross-check of the work count: the fp64 count differs only by pairs
+        # whose q is within rounding of the truncation boundary
+        cpu["support_pairs_oracle"] = oracle_pairs
+        cpu["support_pairs_rel_diff"] = abs(oracle_pairs - support_pairs) / max(oracle_pairs, 1)
 
     f_fwd, f_bwd = flops_per_pair(C)
     kernels = {}

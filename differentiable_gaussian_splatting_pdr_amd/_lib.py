@@ -23,6 +23,7 @@ PDR_ERR_STALE = -5
 EXPORTED = (
     "pdr_splat_tile_size",
     "pdr_splat_bin_variant",
+    "pdr_splat_count_support",
     "pdr_splat_workspace_bytes",
     "pdr_splat_forward",
     "pdr_splat_backward",
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.pdr_splat_tile_size.restype = i
         L.pdr_splat_bin_variant.argtypes = [i, i, i, i]
         L.pdr_splat_bin_variant.restype = i
+        L.pdr_splat_count_support.argtypes = [vp, i, i, i, i, i, f, vp, vp, sz, vp]
+        L.pdr_splat_count_support.restype = i
         L.pdr_splat_workspace_bytes.argtypes = [i, i, i, i, i, ll]
         L.pdr_splat_workspace_bytes.restype = ll
         L.pdr_splat_forward.argtypes = [vp, vp, i, i, i, i, i, f, vp, sz, vp]
@@ -127,6 +130,13 @@ def pdr_splat_tile_size() -> int:
 
 
 PDR_BIN_MEMBERS, PDR_BIN_COLUMNS, PDR_BIN_TWO_LEVEL = 1, 2, 4
+
+
+def pdr_splat_count_support(params, B, N, H, W, C, radius, count, workspace, workspace_bytes,
+                            stream=None) -> int:
+    return _raise(lib().pdr_splat_count_support(params, B, N, H, W, C, float(radius), count,
+                                                workspace, workspace_bytes, stream),
+                  "pdr_splat_count_support")
 
 
 def pdr_splat_bin_variant(B, N, H, W) -> int:

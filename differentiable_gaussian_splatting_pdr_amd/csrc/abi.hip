@@ -262,6 +262,25 @@ int pdr_splat_bin(const float *params, int B, int N, int H, int W, int C, float 
   return hip_status(e);
 }
 
+int pdr_splat_count_support(const float *params, int B, int N, int H, int W, int C, float radius,
+                            unsigned long long *count, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  Dims d;
+  Layout L;
+  if (!params || !count) return PDR_ERR_INVALID_ARG;
+  int rc = validate_sizes(B, N, H, W, C, &d);
+  if (rc == PDR_OK) rc = validate_radius(radius);
+  if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
+  if (rc != PDR_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char *w = (char *)workspace;
+  hipError_t e = launch_binning(params, B, N, H, W, C, radius, workspace, L, (int *)(w + L.tile_off),
+                                (int *)(w + L.list), L.cap, true, st);
+  if (e == hipSuccess)
+    e = launch_count_support(params, B, N, H, W, C, radius, workspace, L, count, st);
+  return hip_status(e);
+}
+
 int pdr_splat_check(void *workspace, void *stream, long long *pairs_needed) {
   if (!workspace) return PDR_ERR_INVALID_ARG;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return PDR_ERR_HIP;

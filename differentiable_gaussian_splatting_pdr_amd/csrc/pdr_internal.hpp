@@ -69,6 +69,10 @@ hipError_t launch_backward_span(const float *params, const void *grad_image, flo
 // output has Cp + C channels per pixel: pixel[b][y][x][0..Cp) first, then the
 // rendered channels (concat fusion).
 // fmt: PDR_FMT_F32 / F16 / BF16 storage of image (concat needs F32).
+// Pairs inside the truncation over the workspace's lists into *count (device).
+hipError_t launch_count_support(const float *params, int B, int N, int H, int W, int C,
+                                float radius, void *ws, const Layout &L,
+                                unsigned long long *count, hipStream_t st);
 hipError_t launch_forward_raster(const float *params, void *image, int B, int N, int H, int W,
                                  int C, float radius, void *ws, const Layout &L, hipStream_t st,
                                  const float *pixel = nullptr, int Cp = 0, int fmt = PDR_FMT_F32);

@@ -264,6 +264,71 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
   }
 }
 
+// Support count: the forward raster's traversal (same lists, staged unit
+// masks and fp32 q' per unit) with the accumulation replaced by a count of
+// the lanes inside the truncation whose pixel lies in the frame (a ragged
+// tile's lanes past the frame edge are evaluated but never stored); one
+// 64-bit atomic per wave.  The number of (Gaussian, pixel) pairs the
+// forward accumulates into the image, used as the work count of throughput
+// figures.
+template <int UW, int UX, int UY>
+__global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_count_support(
+    const GRec *__restrict__ recs, const float *__restrict__ params,
+    const int *__restrict__ tile_off, const int *__restrict__ list, int B, int N, int H, int W,
+    int C, float thr, int nTx, int nT, unsigned long long *__restrict__ count,
+    const WsHeader *hdr) {
+  using WL = WaveLayout<UW, UX, UY>;
+  constexpr int UH = WL::kUH;
+  int f, t;
+  if (!xcd_frame_item(blockIdx.x, nT, B, &f, &t)) return;
+  if (hdr->status & kStatusOverflow) return;
+  __shared__ Entry<1> s[WL::kBatch];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tx0 = (t % nTx) * kTileW, ty0 = (t / nTx) * kTileH;
+  const int ry0 = ty0 + wave * WL::kRH;
+  const int mshift = wave * WL::kUnitsPerWave;
+  const int lx = lane % UW, ly = lane / UW;
+  const float fx = (float)lx + 0.5f, fy = (float)(ry0 - ty0 + ly) + 0.5f;
+  const int P = 5 + C;
+  const size_t gbase = (size_t)f * N;
+  unsigned long long n_in = 0;  // wave-uniform
+  const int beg = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t]);
+  const int end = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t + 1]);
+  for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
+    const int cnt = min(WL::kBatch, end - s0);
+    __syncthreads();
+    stage_entry<1, UW>(s, recs, params, list, s0, cnt, gbase, P, 0, 1, tid, tx0, ty0, thr);
+    __syncthreads();
+    const int ecnt = __builtin_amdgcn_readfirstlane(cnt);
+    for (int e = 0; e < ecnt; ++e) {
+      const Entry<1> r = s[e];
+      const unsigned int um =
+          (__builtin_amdgcn_readfirstlane(r.mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+      if (um == 0u) continue;
+#pragma unroll
+      for (int j = 0; j < UY; ++j) {
+        if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
+        const float dy = (fy + (float)(UH * j)) - r.my;
+        const bool row_in = ry0 + UH * j + ly < H;
+#pragma unroll
+        for (int i = 0; i < UX; ++i) {
+          if (!(um & (1u << (j * UX + i)))) continue;
+          const float dx = (fx + (float)(UW * i)) - r.mx;
+          const float u1 = r.l11 * dx + r.l12 * dy;
+          const float u2 = r.l21 * dx + r.l22 * dy;
+          const float q = u1 * u1 + u2 * u2;
+          const bool in_frame = row_in && tx0 + UW * i + lx < W;
+          n_in += __popcll(__builtin_amdgcn_ballot_w64(q <= thr && in_frame));
+        }
+      }
+    }
+  }
+  if (lane == 0 && n_in) atomicAdd(count, n_in);
+}
+
+__global__ void k_zero_count(unsigned long long *count) { *count = 0ull; }
+
 // Wave reduction through an LDS transpose: every lane writes its K values
 // value-major (row k of red, rows padded to 68 words so that the vector
 // reads below spread over the banks); lane l = g * GL + m (GL = 64 / KP
@@ -617,6 +682,19 @@ hipError_t launch_forward_raster(const float *params, void *image, int B, int N,
     a.iv.xin = (c0 == 0 && Cp > 0) ? pixel : nullptr;   // copied once
     dispatch<false>(a, st);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_count_support(const float *params, int B, int N, int H, int W, int C,
+                                float radius, void *ws, const Layout &L,
+                                unsigned long long *count, hipStream_t st) {
+  const RasterArgs a = raster_args(params, B, N, H, W, C, radius, ws, L);
+  constexpr int UW = PDR_UNIT_W, UX = PDR_UNITS_X, UY = PDR_UNITS_Y;
+  using WL = WaveLayout<UW, UX, UY>;
+  hipLaunchKernelGGL(k_zero_count, dim3(1), dim3(1), 0, st, count);
+  hipLaunchKernelGGL((k_count_support<UW, UX, UY>), dim3((unsigned)xcd_grid(a.nT, a.B)),
+                     dim3(WL::kThreads), 0, st, a.recs, a.params, a.tile_off, a.list, a.B, a.N,
+                     a.H, a.W, a.C, a.thr, a.nTx, a.nT, count, a.hdr);
   return hipGetLastError();
 }
 

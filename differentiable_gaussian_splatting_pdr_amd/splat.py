@@ -141,6 +141,28 @@ def backward(params: torch.Tensor, grad_image: torch.Tensor, H: int, W: int,
     raise _lib.PdrError(rc, "pdr_splat_backward")
 
 
+def count_support(params: torch.Tensor, H: int, W: int, radius: float = 3.0,
+                  workspace: Workspace | None = None) -> int:
+    """(Gaussian, pixel) pairs inside the truncation, counted on the device
+    over the forward raster's traversal (the work of a forward)."""
+    B, N, C = _check_params(params)
+    dev = params.device
+    ws = workspace or Workspace(dev)
+    ws.ensure(Workspace.bytes_for(B, N, H, W, C, _initial_pairs(B, N, H, W)))
+    out = torch.empty(1, dtype=torch.int64, device=dev)
+    st = _stream(dev)
+    for _ in range(2):
+        _lib.pdr_splat_count_support(params.data_ptr(), B, N, H, W, C, radius, out.data_ptr(),
+                                     ws.ptr, ws.nbytes, st)
+        rc, need = _lib.pdr_splat_check(ws.ptr, st)
+        if rc == _lib.PDR_OK:
+            return int(out.item())
+        if rc != _lib.PDR_ERR_OVERFLOW:
+            raise _lib.PdrError(rc, "pdr_splat_count_support")
+        ws.ensure(Workspace.bytes_for(B, N, H, W, C, need))
+    raise _lib.PdrError(_lib.PDR_ERR_OVERFLOW, "pdr_splat_count_support")
+
+
 def bin_lists(params: torch.Tensor, H: int, W: int, radius: float = 3.0):
     """Binning only: returns (tile_off int32 [B*nT+1], tile_list int32 [pairs])."""
     B, N, C = _check_params(params)

@@ -112,6 +112,20 @@ int pdr_splat_bin(const float *params, int B, int N, int H, int W, int C, float 
                   int *tile_off, int *tile_list, long long cap, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/* Work count for throughput figures: bins as pdr_splat_forward does (the
+ * workspace's lists are then reusable by a backward), then walks the same
+ * tile lists, unit masks and fp32 whitened distance as the forward raster
+ * and writes to *count (a device pointer to one unsigned 64-bit integer,
+ * overwritten) the number of (Gaussian, pixel) pairs inside the truncation,
+ * i.e. the pairs the forward accumulates: q <= radius^2 in the definition
+ * at the top of this header, with ties at the boundary decided in fp32 as
+ * the rasters decide them.  Same
+ * validation, workspace and overflow protocol as pdr_splat_forward: *count
+ * is only valid when pdr_splat_check reports PDR_OK. */
+int pdr_splat_count_support(const float *params, int B, int N, int H, int W, int C, float radius,
+                            unsigned long long *count, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 /* Synchronises `stream`, then reports the device-side status of the last
  * call on `workspace`: PDR_OK, PDR_ERR_OVERFLOW or PDR_ERR_STALE (or
  * PDR_ERR_HIP).  *pairs_needed (may be NULL) receives the pair total of the

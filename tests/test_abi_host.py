@@ -203,3 +203,13 @@ def test_bin_variant_validates():
     assert L.pdr_splat_bin_variant(1, 10, 40000, 16) == _lib.PDR_ERR_INVALID_ARG
     with pytest.raises(_lib.PdrError):
         _lib.pdr_splat_bin_variant(1, 0, 16, 16)
+
+
+def test_count_support_validates():
+    L = _lib.lib()
+    # null count, null params, zero frames, bad radius: rejected before any launch
+    assert L.pdr_splat_count_support(FAKE, 1, 4, 16, 16, 1, 3.0, None, FAKE, 1 << 20, None) == -1
+    assert L.pdr_splat_count_support(None, 1, 4, 16, 16, 1, 3.0, FAKE, FAKE, 1 << 20, None) == -1
+    assert L.pdr_splat_count_support(FAKE, 0, 4, 16, 16, 1, 3.0, FAKE, FAKE, 1 << 20, None) == -1
+    assert L.pdr_splat_count_support(FAKE, 1, 4, 16, 16, 1, -1.0, FAKE, FAKE, 1 << 20, None) == -1
+    assert L.pdr_splat_count_support(FAKE, 1, 4, 16, 16, 1, 3.0, FAKE, FAKE, 16, None) == -2
