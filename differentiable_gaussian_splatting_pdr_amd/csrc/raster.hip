@@ -445,9 +445,17 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
   constexpr bool kXpose = UseXpose<CP>::value;
   __shared__ __align__(16) float red_all[kXpose ? WL::kWaves * KP * kRedRow : 1];
   float *red = red_all + (kXpose ? wave * KP * kRedRow : 0);  // this wave's rows
-  const int vidx = kXpose ? lane / (kWave / KP) : value_index<KP>(lane);
-  int slot = -1;
-  if (kXpose ? lane % (kWave / KP) == 0 : reduce_issuer<KP>(lane)) {
+  // With 16 channels the 21 sums would fill a 32-value butterfly with 11
+  // zeros; instead the amplitude sums take a 16-value one and the five
+  // moments an 8-value one (53 instead of 70 VALU per entry, a second
+  // atomic instruction).
+  constexpr bool kSplit = CP == 16;
+  const int vidx = kXpose ? lane / (kWave / KP) : value_index<kSplit ? 16 : KP>(lane);
+  int slot = -1, slot_m = -1;
+  if constexpr (kSplit) {
+    if (reduce_issuer<16>(lane)) slot = vidx < cc ? 5 + c0 + vidx : -1;
+    if (reduce_issuer<8>(lane) && value_index<8>(lane) < 5) slot_m = value_index<8>(lane);
+  } else if (kXpose ? lane % (kWave / KP) == 0 : reduce_issuer<KP>(lane)) {
     if (vidx < CP) slot = vidx < cc ? 5 + c0 + vidx : -1;
     else if (vidx < K) slot = vidx - CP;
   }
@@ -515,10 +523,18 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
       };
       for_units_from_first<WL::kUnitsPerWave>(um, unit);
       if (!any) continue;
-      float tot;
-      if constexpr (kXpose) tot = wave_reduce_xpose<K, KP>(part, red, lane);
-      else tot = wave_reduce_transposed<KP>(part, lane);
-      if (slot >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot), tot);
+      if constexpr (kSplit) {
+        // part[16..20] are the moments, part[21..23] zero
+        const float tot = wave_reduce_transposed<16>(part, lane);
+        const float tot_m = wave_reduce_transposed<8>(part + 16, lane);
+        if (slot >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot), tot);
+        if (slot_m >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot_m), tot_m);
+      } else {
+        float tot;
+        if constexpr (kXpose) tot = wave_reduce_xpose<K, KP>(part, red, lane);
+        else tot = wave_reduce_transposed<KP>(part, lane);
+        if (slot >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot), tot);
+      }
     }
   }
 }
