@@ -148,12 +148,15 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
 //                   and compaction on its own members only, which wins when
 //                   a frame has many bands.
 //
-// Count pass (WRITE = false): per-tile counts and the group's total.
+// Count pass (WRITE = false): per-tile counts -- one LDS atomic add per
+// (box, group tile) overlap, over the boxes the group would scan -- and the
+// group's total.
 // Write pass (WRITE = true): the group's base offset is the sum of the
 // totals of all groups before it (frame-major, bands top to bottom); an
 // exclusive scan (wave64 DPP scan) of its tiles' counts gives their
-// offsets; then the lists are written.  The last group writes the pair
-// total and the overflow flag.  Both passes form the same chunks.
+// offsets; then the lists are written through the chunks above.  The last
+// group writes the pair total and the overflow flag.  A tile's list length
+// is the number of boxes that meet it either way.
 constexpr int kSegSlots = 4;   // boxes per thread per member-scan segment
 
 template <bool WRITE, bool MEMBERS, bool COLS, bool ROWL = false>
@@ -301,109 +304,140 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
     }
   };
 
-  for (int w = tid; w < Tg * words; w += kBinThreads) bits[w] = 0u;
-
-  if constexpr (!MEMBERS) {
-    // chunks of NC consecutive Gaussians, loaded all at once one chunk ahead
-    constexpr int kPer = kMaxChunk / kBinThreads;
-    uint2 nxt[kPer];
-    auto load_chunk = [&](int c) {
+  if constexpr (!WRITE) {
+    // The count pass needs no order: every (box, group tile) overlap adds
+    // one to the tile's count -- the same integers the write pass's bit
+    // matrix yields, with no matrix and no compaction.
+    __syncthreads();  // base cleared
+    for (int j0 = 0; j0 < rn; j0 += kSegSlots * kBinThreads) {
+      // kSegSlots boxes per thread in flight at once (list entries first)
+      int n[kSegSlots];
+      uint2 bx[kSegSlots];
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int i = tid + k * kBinThreads;
-        nxt[k] = (i < NC && c + i < N) ? fb[c + i] : make_uint2(kEmptyBox, kEmptyBox);
+      for (int k = 0; k < kSegSlots; ++k) {
+        const int j = j0 + k * kBinThreads + tid;
+        n[k] = j;
+        if constexpr (ROWL) n[k] = (rl && j < rn) ? rl[j] : j;
       }
-    };
-    load_chunk(0);
-    for (int c0 = 0; c0 < N; c0 += NC) {
-      uint2 cur[kPer];
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) cur[k] = nxt[k];
-      __syncthreads();  // bits clear
-      if (c0 + NC < N) load_chunk(c0 + NC);
+      for (int k = 0; k < kSegSlots; ++k)
+        bx[k] = j0 + k * kBinThreads + tid < rn ? fb[n[k]] : make_uint2(kEmptyBox, kEmptyBox);
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) set_bits(tid + k * kBinThreads, cur[k]);
-      __syncthreads();
-      compact(min(NC, N - c0 + 31) >> 5, [&](int j) { return c0 + j; });
+      for (int k = 0; k < kSegSlots; ++k) {
+        const int x0 = (int)(bx[k].x & 0xffffu), x1 = (int)(bx[k].x >> 16);
+        const int y0 = (int)(bx[k].y & 0xffffu), y1 = (int)(bx[k].y >> 16);
+        if (x0 > x1) continue;
+        const int ux0 = max(x0 >> kTileShiftX, cx0), ux1 = min(x1 >> kTileShiftX, cx0 + aw - 1);
+        const int uy0 = max(y0 >> kTileShiftY, ty0), uy1 = min(y1 >> kTileShiftY, ty0 + ah - 1);
+        for (int ty = uy0; ty <= uy1; ++ty)
+          for (int tx = ux0; tx <= ux1; ++tx) atomicAdd(&base[(ty - ty0) * aw + (tx - cx0)], 1);
+      }
     }
   } else {
-    // the members [0, cnt) form a chunk
-    auto flush = [&](int cnt) {
-      __syncthreads();  // member list complete, bits clear
-      for (int j = tid; j < cnt; j += kBinThreads) set_bits(j, fb[mem[j]]);
-      __syncthreads();
-      compact((cnt + 31) >> 5, [&](int j) { return mem[j]; });
-      __syncthreads();  // the member list is refilled next
-    };
-    bool direct = false;
-    if constexpr (ROWL && !COLS) direct = rl != nullptr;
-    if (direct) {
-      // a whole tile row: every entry of the row's list meets the group
-      for (int c0 = 0; c0 < rn; c0 += NC) {
-        const int cnt = min(NC, rn - c0);
-        for (int j = tid; j < cnt; j += kBinThreads) mem[j] = rl[c0 + j];
-        flush(cnt);
-      }
-    } else {
-      const int S = min(NC, kSegSlots * kBinThreads);  // boxes per segment
-      uint2 nxt[kSegSlots];
-      int nid[kSegSlots];   // ROWL: the Gaussian indices of the prefetched boxes
-      auto load_seg = [&](int s0) {
+    for (int w = tid; w < Tg * words; w += kBinThreads) bits[w] = 0u;
+
+    if constexpr (!MEMBERS) {
+      // chunks of NC consecutive Gaussians, loaded all at once one chunk ahead
+      constexpr int kPer = kMaxChunk / kBinThreads;
+      uint2 nxt[kPer];
+      auto load_chunk = [&](int c) {
   #pragma unroll
-        for (int k = 0; k < kSegSlots; ++k) {
-          const int o = k * kBinThreads + tid;
-          const bool v = o < S && s0 + o < rn;
-          if constexpr (ROWL) {
-            nid[k] = v ? (rl ? rl[s0 + o] : s0 + o) : 0;
-            nxt[k] = v ? fb[nid[k]] : make_uint2(kEmptyBox, kEmptyBox);
-          } else {
-            nxt[k] = v ? fb[s0 + o] : make_uint2(kEmptyBox, kEmptyBox);
-          }
+        for (int k = 0; k < kPer; ++k) {
+          const int i = tid + k * kBinThreads;
+          nxt[k] = (i < NC && c + i < N) ? fb[c + i] : make_uint2(kEmptyBox, kEmptyBox);
         }
       };
-      load_seg(0);
-      int cnt = 0;  // members gathered for the current chunk (uniform)
-      for (int s0 = 0; s0 < rn; s0 += S) {
-        bool in[kSegSlots];
-        unsigned long long bal[kSegSlots];
-        int cid[kSegSlots];
+      load_chunk(0);
+      for (int c0 = 0; c0 < N; c0 += NC) {
+        uint2 cur[kPer];
   #pragma unroll
-        for (int k = 0; k < kSegSlots; ++k) {
-          cid[k] = ROWL ? nid[k] : s0 + k * kBinThreads + tid;
-          const uint2 bx = nxt[k];
-          const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
-          const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
-          in[k] = x0 <= x1 && (y0 >> kTileShiftY) < ty0 + ah && (y1 >> kTileShiftY) >= ty0 &&
-                  (!COLS || ((x0 >> kTileShiftX) < cx0 + aw && (x1 >> kTileShiftX) >= cx0));
-          bal[k] = __builtin_amdgcn_ballot_w64(in[k]);
-          if (lane == 0) wcnt[k][wave] = __popcll(bal[k]);
-        }
-        if (s0 + S < rn) load_seg(s0 + S);
+        for (int k = 0; k < kPer; ++k) cur[k] = nxt[k];
+        __syncthreads();  // bits clear
+        if (c0 + NC < N) load_chunk(c0 + NC);
+  #pragma unroll
+        for (int k = 0; k < kPer; ++k) set_bits(tid + k * kBinThreads, cur[k]);
         __syncthreads();
-        // members of this segment, in index order (slot-major, then wave, lane)
-        int total = 0, before[kSegSlots];
-  #pragma unroll
-        for (int k = 0; k < kSegSlots; ++k) {
-          int wsum = 0, wpre = 0;
-          for (int w = 0; w < kBinThreads / kWave; ++w) {
-            wpre += w < wave ? wcnt[k][w] : 0;
-            wsum += wcnt[k][w];
-          }
-          before[k] = total + wpre;
-          total += wsum;
-        }
-        if (cnt + total > NC) {  // total <= S <= NC
-          flush(cnt);
-          cnt = 0;
-        }
-        const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  #pragma unroll
-        for (int k = 0; k < kSegSlots; ++k)
-          if (in[k]) mem[cnt + before[k] + __popcll(bal[k] & lt_mask)] = cid[k];
-        cnt += total;
-        __syncthreads();  // wcnt is rewritten by the next segment
+        compact(min(NC, N - c0 + 31) >> 5, [&](int j) { return c0 + j; });
       }
-      if (cnt > 0) flush(cnt);
+    } else {
+      // the members [0, cnt) form a chunk
+      auto flush = [&](int cnt) {
+        __syncthreads();  // member list complete, bits clear
+        for (int j = tid; j < cnt; j += kBinThreads) set_bits(j, fb[mem[j]]);
+        __syncthreads();
+        compact((cnt + 31) >> 5, [&](int j) { return mem[j]; });
+        __syncthreads();  // the member list is refilled next
+      };
+      bool direct = false;
+      if constexpr (ROWL && !COLS) direct = rl != nullptr;
+      if (direct) {
+        // a whole tile row: every entry of the row's list meets the group
+        for (int c0 = 0; c0 < rn; c0 += NC) {
+          const int cnt = min(NC, rn - c0);
+          for (int j = tid; j < cnt; j += kBinThreads) mem[j] = rl[c0 + j];
+          flush(cnt);
+        }
+      } else {
+        const int S = min(NC, kSegSlots * kBinThreads);  // boxes per segment
+        uint2 nxt[kSegSlots];
+        int nid[kSegSlots];   // ROWL: the Gaussian indices of the prefetched boxes
+        auto load_seg = [&](int s0) {
+    #pragma unroll
+          for (int k = 0; k < kSegSlots; ++k) {
+            const int o = k * kBinThreads + tid;
+            const bool v = o < S && s0 + o < rn;
+            if constexpr (ROWL) {
+              nid[k] = v ? (rl ? rl[s0 + o] : s0 + o) : 0;
+              nxt[k] = v ? fb[nid[k]] : make_uint2(kEmptyBox, kEmptyBox);
+            } else {
+              nxt[k] = v ? fb[s0 + o] : make_uint2(kEmptyBox, kEmptyBox);
+            }
+          }
+        };
+        load_seg(0);
+        int cnt = 0;  // members gathered for the current chunk (uniform)
+        for (int s0 = 0; s0 < rn; s0 += S) {
+          bool in[kSegSlots];
+          unsigned long long bal[kSegSlots];
+          int cid[kSegSlots];
+    #pragma unroll
+          for (int k = 0; k < kSegSlots; ++k) {
+            cid[k] = ROWL ? nid[k] : s0 + k * kBinThreads + tid;
+            const uint2 bx = nxt[k];
+            const int x0 = (int)(bx.x & 0xffffu), x1 = (int)(bx.x >> 16);
+            const int y0 = (int)(bx.y & 0xffffu), y1 = (int)(bx.y >> 16);
+            in[k] = x0 <= x1 && (y0 >> kTileShiftY) < ty0 + ah && (y1 >> kTileShiftY) >= ty0 &&
+                    (!COLS || ((x0 >> kTileShiftX) < cx0 + aw && (x1 >> kTileShiftX) >= cx0));
+            bal[k] = __builtin_amdgcn_ballot_w64(in[k]);
+            if (lane == 0) wcnt[k][wave] = __popcll(bal[k]);
+          }
+          if (s0 + S < rn) load_seg(s0 + S);
+          __syncthreads();
+          // members of this segment, in index order (slot-major, then wave, lane)
+          int total = 0, before[kSegSlots];
+    #pragma unroll
+          for (int k = 0; k < kSegSlots; ++k) {
+            int wsum = 0, wpre = 0;
+            for (int w = 0; w < kBinThreads / kWave; ++w) {
+              wpre += w < wave ? wcnt[k][w] : 0;
+              wsum += wcnt[k][w];
+            }
+            before[k] = total + wpre;
+            total += wsum;
+          }
+          if (cnt + total > NC) {  // total <= S <= NC
+            flush(cnt);
+            cnt = 0;
+          }
+          const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    #pragma unroll
+          for (int k = 0; k < kSegSlots; ++k)
+            if (in[k]) mem[cnt + before[k] + __popcll(bal[k] & lt_mask)] = cid[k];
+          cnt += total;
+          __syncthreads();  // wcnt is rewritten by the next segment
+        }
+        if (cnt > 0) flush(cnt);
+      }
     }
   }
   __syncthreads();
