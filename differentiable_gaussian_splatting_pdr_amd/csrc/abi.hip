@@ -116,7 +116,9 @@ int backward_impl(const float *params, const void *grad_image, int Cp, float *gr
   char *w = (char *)workspace;
   hipError_t e = hipSuccess;
   if (span) {
-    if (!reuse_binning) e = launch_preprocess(params, B, N, H, W, C, radius, workspace, L, true, st);
+    // records only, no tile lists: the workspace is not stamped as holding
+    // a binning, so a later reuse of it is reported stale
+    if (!reuse_binning) e = launch_preprocess(params, B, N, H, W, C, radius, workspace, L, false, st);
     if (e == hipSuccess)
       e = launch_backward_span(params, grad_image, grad_params, B, N, H, W, C, radius, workspace, L,
                                reuse_binning != 0, st, fmt);

@@ -124,6 +124,35 @@ def test_span_stale_and_rejects():
                                      wl.W, wl.C, 3.0, ws.ptr, ws.nbytes, 0, 7, None) == -1
 
 
+def test_span_rebin_leaves_no_reusable_binning(orc):
+    # a span backward that rebins builds records but no tile lists: a later
+    # tile backward that asks to reuse the workspace's binning must be told
+    # it is stale (not run on the lists of an earlier forward)
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import _lib, splat
+    wl, p, g = workloads.make_inputs(1, frames=2)
+    dev = torch.device("cuda:0")
+    pt = torch.from_numpy(p).to(dev)
+    _, ws = splat.forward(pt, wl.H, wl.W)          # lists for these params
+    gt = torch.from_numpy(g).to(dev)
+    gp = torch.empty_like(pt)
+    st = torch.cuda.current_stream().cuda_stream
+    B = pt.shape[0]
+    _lib.pdr_splat_backward_algo(pt.data_ptr(), gt.data_ptr(), 0, gp.data_ptr(), B, wl.N, wl.H,
+                                 wl.W, wl.C, 3.0, ws.ptr, ws.nbytes, 0, span(), st)
+    assert _lib.pdr_splat_check(ws.ptr, st)[0] == _lib.PDR_OK
+    _lib.pdr_splat_backward_algo(pt.data_ptr(), gt.data_ptr(), 0, gp.data_ptr(), B, wl.N, wl.H,
+                                 wl.W, wl.C, 3.0, ws.ptr, ws.nbytes, 1, _lib.PDR_BWD_TILE, st)
+    assert _lib.pdr_splat_check(ws.ptr, st)[0] == _lib.PDR_ERR_STALE
+    # a forward restores a reusable binning
+    splat.forward(pt, wl.H, wl.W, workspace=ws)
+    _lib.pdr_splat_backward_algo(pt.data_ptr(), gt.data_ptr(), 0, gp.data_ptr(), B, wl.N, wl.H,
+                                 wl.W, wl.C, 3.0, ws.ptr, ws.nbytes, 1, _lib.PDR_BWD_TILE, st)
+    assert _lib.pdr_splat_check(ws.ptr, st)[0] == _lib.PDR_OK
+    gr, gsl, gmag = orc.grad(p, g, wl.H, wl.W)
+    check_close(gp.cpu().numpy(), gr, gmag, gsl, "grad after a fresh forward")
+
+
 def test_auto_choice(orc):
     # the library default takes the span walk for small problems (B*N <= 32768)
     # and the tile raster beyond; the span walk is deterministic (no atomics),
