@@ -52,16 +52,25 @@ __device__ __forceinline__ float clamp_to_float(double v) {
 // are read with coalesced loads, the first five values of every row staged
 // in LDS and any non-finite value flagged, then each thread builds one
 // Gaussian's record.
+constexpr int kZeroBlocks = 32;   // preprocess blocks at least (for clearing the order histogram)
+
 __global__ __launch_bounds__(256) void k_preprocess(const float *__restrict__ params, int BN, int C,
                                                     FastDiv pdiv, int H, int W, float radius,
                                                     GRec *__restrict__ recs,
                                                     uint2 *__restrict__ boxes, WsHeader *hdr,
-                                                    int stamp_N, unsigned long long stamp_ptr) {
+                                                    int stamp_N, unsigned long long stamp_ptr,
+                                                    int *__restrict__ ohist) {
   __shared__ float s5[5][256];
   __shared__ int bad[256];
   const int tid = threadIdx.x;
   const int g0 = blockIdx.x * 256;
   const int i = g0 + tid;
+  // the tile-order histogram the binning's count pass fills, if any (the
+  // grid then has at least kZeroBlocks blocks; those past the Gaussians only
+  // clear it)
+  if (ohist)
+    for (int j = i; j < 8 * kOrderBuckets; j += gridDim.x * 256) ohist[j] = 0;
+  if (g0 >= BN) return;  // uniform per block
   if (i == 0) {
     hdr->stamp[0] = BN / stamp_N;
     hdr->stamp[1] = stamp_N;
@@ -166,7 +175,8 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
                                                      int *__restrict__ gtot,
                                                      int *__restrict__ tile_off,
                                                      int *__restrict__ list, long long cap,
-                                                     WsHeader *hdr,
+                                                     WsHeader *hdr, int *__restrict__ ohist,
+                                                     int *__restrict__ order,
                                                      const int *__restrict__ rlist = nullptr,
                                                      const int *__restrict__ fstart = nullptr,
                                                      long long rcap = 0) {
@@ -241,6 +251,16 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
     if (2 * tid + 1 < Tg) {
       tile_off[t0 + 2 * tid + 1] = (int)min(e0 + c0, 0x7fffffffLL);
       base[2 * tid + 1] = (int)min(e0 + c0, 0x7fffffffLL);
+    }
+    // longest-first raster order: each tile takes the next slot of its
+    // (XCD range, length bucket); the cursors come from k_order_scan
+    if (ohist) {
+      const unsigned int total = (unsigned int)B * (unsigned int)nT;
+      for (int k = 0; k < 2; ++k) {
+        if (2 * tid + k >= Tg) break;
+        const unsigned int gt = (unsigned int)(t0 + 2 * tid + k);
+        order[atomicAdd(&ohist[order_slot(gt, total, k ? c1 : c0)], 1)] = (int)gt;
+      }
     }
     const long long gend = gbase + gsum;
     const bool limit = gend > cap || gend > 0x7fffffffLL;
@@ -443,9 +463,12 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
   __syncthreads();
   if (!WRITE) {
     long long part = 0;
+    const unsigned int total = (unsigned int)B * (unsigned int)nT;
     for (int lt = tid; lt < Tg; lt += kBinThreads) {
       counts[t0 + lt] = base[lt];
       part += base[lt];
+      // histogram of the tiles' order keys per XCD range
+      if (ohist) atomicAdd(&ohist[order_slot((unsigned int)(t0 + lt), total, base[lt])], 1);
     }
     const long long tot = block_sum_ll(part, red);
     if (tid == 0) gtot[(size_t)b * G + g] = (int)min(tot, 0x7fffffffLL);
@@ -603,6 +626,35 @@ __global__ __launch_bounds__(kBinThreads) void k_rowstart(int nTy, int *__restri
   if (tid == 0) fs[nTy] = (int)min(carry, 0x7fffffffLL);
 }
 
+// One workgroup per XCD range: exclusive scan of the range's key histogram
+// (keys ascending: longest first) in place, plus the range's first slot,
+// so that each entry becomes the next free position of its key in order[].
+constexpr int kOrderPer = kOrderBuckets / kBinThreads;
+static_assert(kOrderBuckets % kBinThreads == 0, "whole keys per thread");
+__global__ __launch_bounds__(kBinThreads) void k_order_scan(int *__restrict__ ohist,
+                                                            unsigned int total) {
+  __shared__ int wtot[kBinThreads / kWave];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int *h = ohist + r * kOrderBuckets;
+  int v[kOrderPer], t = 0;
+#pragma unroll
+  for (int k = 0; k < kOrderPer; ++k) {
+    v[k] = h[tid * kOrderPer + k];
+    t += v[k];
+  }
+  const int incl = wave_incl_scan(t);
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int wex = 0;
+  for (int w = 0; w < wave; ++w) wex += wtot[w];
+  int e = (int)((unsigned int)r * ((total + 7u) >> 3)) + wex + incl - t;
+#pragma unroll
+  for (int k = 0; k < kOrderPer; ++k) {
+    h[tid * kOrderPer + k] = e;
+    e += v[k];
+  }
+}
+
 // ----------------------------------------------------------------------------
 // host launchers
 
@@ -753,12 +805,16 @@ hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, in
                              void *ws, const Layout &L, bool stamp_valid, hipStream_t st) {
   char *w = (char *)ws;
   long long BN = (long long)B * N;
+  const bool ordered = tile_order_on((long long)B * ((W + kTileW - 1) / kTileW) *
+                                     ((H + kTileH - 1) / kTileH));
+  const long long blocks = std::max((BN + 255) / 256, ordered ? (long long)kZeroBlocks : 1LL);
   PDR_TIMED(PDR_K_PREPROCESS, st,
-            hipLaunchKernelGGL(k_preprocess, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,
+            hipLaunchKernelGGL(k_preprocess, dim3((unsigned)blocks), dim3(256), 0, st,
                                params, (int)BN, C, make_fastdiv((uint32_t)(5 + C)), H, W, radius,
                                (GRec *)(w + L.recs),
                                (uint2 *)(w + L.boxes), (WsHeader *)(w + L.hdr), N,
-                               stamp_valid ? (unsigned long long)(uintptr_t)params : 0ull));
+                               stamp_valid ? (unsigned long long)(uintptr_t)params : 0ull,
+                               ordered ? (int *)(w + L.ohist) : (int *)nullptr));
   return hipGetLastError();
 }
 
@@ -773,6 +829,9 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
   int *gtot = (int *)(w + L.gtot);
   long long BN = (long long)B * N;
   int nTx = (W + kTileW - 1) / kTileW, nTy = (H + kTileH - 1) / kTileH;
+  const bool ordered = tile_order_on((long long)B * nTx * nTy);
+  int *ohist = ordered ? (int *)(w + L.ohist) : nullptr;
+  int *order = ordered ? (int *)(w + L.order) : nullptr;
   const hipError_t pe = launch_preprocess(params, B, N, H, W, C, radius, ws, L, stamp_valid, st);
   if (pe != hipSuccess) return pe;
   const BinPlan plan = plan_binning(B, N, H, W);
@@ -801,12 +860,16 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
                          rp.nblk, rcnt, (const int *)fstart, rlist, L.cap);
       hipLaunchKernelGGL(k_count, g2, dim3(kBinThreads), lds2, st, boxes, B, N, nTx, nTy, 1,
                          bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr, (int *)nullptr,
-                         cap, hdr, (const int *)rlist, (const int *)fstart, L.cap);
+                         cap, hdr, ohist, order, (const int *)rlist, (const int *)fstart, L.cap);
+      if (ordered)
+        hipLaunchKernelGGL(k_order_scan, dim3(8), dim3(kBinThreads), 0, st, ohist,
+                           (unsigned)(B * nTx * nTy));
     });
     PDR_TIMED(PDR_K_BIN_WRITE, st,
               hipLaunchKernelGGL(k_write, g2, dim3(kBinThreads), lds2, st, boxes, B, N, nTx, nTy,
                                  1, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, tile_off, list, cap,
-                                 hdr, (const int *)rlist, (const int *)fstart, L.cap));
+                                 hdr, ohist, order, (const int *)rlist, (const int *)fstart,
+                                 L.cap));
     return hipGetLastError();
   }
   const BinGroups &bg = plan.bg;
@@ -819,15 +882,19 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
                          : (cols ? k_bin<false, false, true> : k_bin<false, false, false>);
   auto k_write = members ? (cols ? k_bin<true, true, true> : k_bin<true, true, false>)
                          : (cols ? k_bin<true, false, true> : k_bin<true, false, false>);
-  PDR_TIMED(PDR_K_BIN_COUNT, st,
-            hipLaunchKernelGGL(k_count, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,
-                               bg.gh, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr,
-                               (int *)nullptr, cap, hdr, (const int *)nullptr,
-                               (const int *)nullptr, 0LL));
+  PDR_TIMED(PDR_K_BIN_COUNT, st, {
+    hipLaunchKernelGGL(k_count, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy, bg.gh,
+                       bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr, (int *)nullptr,
+                       cap, hdr, ohist, order, (const int *)nullptr, (const int *)nullptr, 0LL);
+    if (ordered)
+      hipLaunchKernelGGL(k_order_scan, dim3(8), dim3(kBinThreads), 0, st, ohist,
+                         (unsigned)(B * nTx * nTy));
+  });
   PDR_TIMED(PDR_K_BIN_WRITE, st,
             hipLaunchKernelGGL(k_write, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,
                                bg.gh, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, tile_off, list, cap,
-                               hdr, (const int *)nullptr, (const int *)nullptr, 0LL));
+                               hdr, ohist, order, (const int *)nullptr, (const int *)nullptr,
+                               0LL));
   return hipGetLastError();
 }
 

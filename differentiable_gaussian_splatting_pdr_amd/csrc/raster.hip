@@ -182,12 +182,14 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
     const GRec *__restrict__ recs, const float *__restrict__ params,
     const int *__restrict__ tile_off, const int *__restrict__ list, int B, int N, int H, int W,
     int C, int c0, int cc, float thr, int nTx, int nT, void *__restrict__ image, ImgView iv,
-    const WsHeader *hdr) {
+    const WsHeader *hdr, const int *__restrict__ order) {
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
   int f, t;
-  if (!xcd_frame_item(blockIdx.x, nT, B, &f, &t)) return;
-  if (hdr->status & kStatusOverflow) return;
+  if (hdr->status & kStatusOverflow) return;  // (the order is only complete without overflow)
+  if (order ? !ordered_tile(blockIdx.x, nT, B, order, &f, &t)
+            : !xcd_frame_item(blockIdx.x, nT, B, &f, &t))
+    return;
   __shared__ Entry<CP> s[WL::kBatch];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
@@ -402,14 +404,17 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
     const GRec *__restrict__ recs, const float *__restrict__ params,
     const void *__restrict__ gimg, const int *__restrict__ tile_off,
     const int *__restrict__ list, int B, int N, int H, int W, int C, int c0, int cc, float thr,
-    int nTx, int nT, float *__restrict__ sums, ImgView iv, const WsHeader *hdr) {
+    int nTx, int nT, float *__restrict__ sums, ImgView iv, const WsHeader *hdr,
+    const int *__restrict__ order) {
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
   constexpr int K = CP + 5;
   constexpr int KP = Pow2Up<K>::value;
   int f, t;
-  if (!xcd_frame_item(blockIdx.x, nT, B, &f, &t)) return;
   if (hdr->status & (kStatusOverflow | kStatusStale)) return;
+  if (order ? !ordered_tile(blockIdx.x, nT, B, order, &f, &t)
+            : !xcd_frame_item(blockIdx.x, nT, B, &f, &t))
+    return;
   __shared__ Entry<CP> s[WL::kBatch];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
@@ -609,16 +614,27 @@ struct RasterArgs {
   void *out;
   ImgView iv;
   const WsHeader *hdr;
+  const int *order;
+};
+
+// Both rasters take their tiles longest list first (the binning's order),
+// except the 16-channel forward: each of its entries stages 64 bytes of
+// amplitudes, and frame-major dispatch keeps a frame's in L2 -- measured 4%
+// faster there, while its backward gains 6% from the order.
+template <int CP>
+struct ForwardOrdered {
+  static constexpr bool value = CP < 16;
 };
 
 template <int CP, int UW, int UX, int UY>
 void fwd_cp(const RasterArgs &a, hipStream_t st) {
   using WL = WaveLayout<UW, UX, UY>;
   dim3 grid((unsigned)xcd_grid(a.nT, a.B));
+  const int *order = ForwardOrdered<CP>::value ? a.order : nullptr;
   PDR_TIMED(PDR_K_FORWARD_RASTER, st,
             hipLaunchKernelGGL((k_forward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
                                a.recs, a.params, a.tile_off, a.list, a.B, a.N, a.H, a.W, a.C,
-                               a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr));
+                               a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr, order));
 }
 
 template <int CP, int UW, int UX, int UY>
@@ -629,7 +645,7 @@ void bwd_cp(const RasterArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((k_backward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
                                a.recs, a.params, a.gimg, a.tile_off, a.list, a.B, a.N, a.H, a.W,
                                a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, static_cast<float *>(a.out),
-                               a.iv, a.hdr));
+                               a.iv, a.hdr, a.order));
 }
 
 // Unit shape and units per wave (compile-time tuning knob): 8x8 quads,
@@ -681,6 +697,7 @@ RasterArgs raster_args(const float *params, int B, int N, int H, int W, int C, f
   a.out = nullptr;
   a.iv = ImgView{C, 0, nullptr, nullptr, 0, PDR_FMT_F32};
   a.hdr = (const WsHeader *)(w + L.hdr);
+  a.order = tile_order_on((long long)B * a.nT) ? (const int *)(w + L.order) : nullptr;
   return a;
 }
 

@@ -71,9 +71,9 @@ int pdr_splat_bin_variant(int B, int N, int H, int W);
 
 /* Bytes of workspace for a problem and a (tile, Gaussian) pair capacity.
  * Returns a negative pdr_status on invalid sizes.  The fixed part covers a
- * 256-byte header, 40 bytes per Gaussian and 12 bytes per tile (each
- * region rounded up to 256 bytes); every pair takes 4 more
- * bytes.  max_pairs <= 2^31 - 1.
+ * 256-byte header, 40 bytes per Gaussian, 16 bytes per tile and 256 KiB for
+ * ordering the tiles by list length (each region rounded up to 256 bytes);
+ * every pair takes 4 more bytes.  max_pairs <= 2^31 - 1.
  * Problems with many Gaussians per frame on frames of many tile bands
  * (N >= 16384 where a frame's bands would each scan all of its boxes) bin
  * in two levels: first per tile row, then per tile from the row's list.

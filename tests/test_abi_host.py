@@ -50,14 +50,17 @@ def test_workspace_bytes_layout():
     B, N, H, W, C = 384, 4096, 128, 128, 3
     t = _lib.pdr_splat_tile_size()
     bt = B * (128 // t) ** 2
-    fixed = a(256) + a(B * N * 32) + a(B * N * 8) + a(bt * 4) + a(bt * 4) + a((bt + 1) * 4)
+    # header, records, boxes, tile counts, group totals, tile offsets, tile
+    # order, order histogram (8 XCD ranges x 512 length buckets x 16 windows)
+    fixed = (a(256) + a(B * N * 32) + a(B * N * 8) + a(bt * 4) + a(bt * 4) + a((bt + 1) * 4)
+             + a(bt * 4) + 262144)
     assert _lib.pdr_splat_workspace_bytes(B, N, H, W, C, 0) == fixed
     assert _lib.pdr_splat_workspace_bytes(B, N, H, W, C, 1000) == fixed + a(4000)
     # ragged sizes round the tile grid up
     t = _lib.pdr_splat_tile_size()
     nt = ((17 + t - 1) // t) * ((65 + t - 1) // t)
     assert _lib.pdr_splat_workspace_bytes(1, 10, 17, 65, 1, 0) == (
-        a(256) + a(320) + a(80) + a(nt * 4) + a(nt * 4) + a((nt + 1) * 4))
+        a(256) + a(320) + a(80) + a(nt * 4) + a(nt * 4) + a((nt + 1) * 4) + a(nt * 4) + 262144)
 
 
 @pytest.mark.parametrize("args", [
