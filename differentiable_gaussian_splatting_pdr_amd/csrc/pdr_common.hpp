@@ -53,13 +53,35 @@ static_assert(sizeof(GRec) == 32, "record is 32 bytes");
 constexpr unsigned int kEmptyBox = 0x0000FFFFu;  // x0 = 65535 > x1 = 0
 
 // Rasters take their tiles longest list first within each XCD's share of
-// the grid: a counting sort of the tiles by list length.  Keys per XCD
-// range: kOrderLen length buckets (exact below 256 entries, then 8 entries
-// wide up to 2303, longer lists share the last), each split into kOrderSub
-// position windows of the range so that tiles of equal length stay in
-// roughly frame order (keeping a frame's records together in L2).
-constexpr int kOrderLen = 512, kOrderSub = 16;
-constexpr int kOrderBuckets = kOrderLen * kOrderSub;   // keys per XCD range
+// the grid: a counting sort of the tiles by a key made of the list
+// length's octave (floor(log2(len + 1)), longest first, 16 classes), its
+// quarter of the octave (longest first), the tile's position window in the
+// range (kOrderSub windows), then the length within the quarter.  The
+// longest tiles of a range -- the ones that would form the tail -- go
+// first wherever they are; tiles of similar length sweep the range in
+// frame order, which keeps a frame's records together in L2.
+#ifndef PDR_ORDER_QUARTERS
+#define PDR_ORDER_QUARTERS 4
+#endif
+constexpr int kOrderClasses = 16, kOrderSub = 16, kOrderFine = 32;
+constexpr int kOrderQ = PDR_ORDER_QUARTERS;   // length steps of an octave taken before the windows
+constexpr int kOrderBuckets = kOrderClasses * kOrderSub * kOrderFine;   // keys per XCD range
+
+// Key of a tile with list length len at offset pos of its XCD range of per
+// tiles (0 <= key < kOrderBuckets; a longer list never gets a larger key
+// within a window).
+__device__ __forceinline__ int order_key(int len, unsigned int pos, unsigned int per) {
+  const unsigned int l1 = (unsigned int)len + 1u;               // >= 1
+  const int cls = min(kOrderClasses - 1, 31 - __clz((int)l1));  // floor(log2(len + 1))
+  const unsigned int lo = (1u << cls) - 1u;                     // len in [lo, 2 lo + 1] below the cap
+  const int fine = (int)min((unsigned int)kOrderFine - 1u,
+                            (((unsigned int)len - lo) * (unsigned int)kOrderFine) >> cls);
+  const int sub = (int)(((unsigned long long)pos * kOrderSub) / per);
+  constexpr int kF = kOrderFine / kOrderQ;            // fine steps within a quarter
+  const int q = fine / kF, f = fine - q * kF;
+  return (((kOrderClasses - 1 - cls) * kOrderQ + (kOrderQ - 1 - q)) * kOrderSub + sub) * kF +
+         (kF - 1 - f);
+}
 
 // The order costs a launch and a histogram clear (~4 us).  It paid at
 // 2560 tiles (160 frames of 64x64: both rasters 6-10% faster, though all
@@ -67,14 +89,6 @@ constexpr int kOrderBuckets = kOrderLen * kOrderSub;   // keys per XCD range
 // but not at 16 (one 64x64 frame).
 constexpr long long kOrderMinTiles = 1024;
 inline bool tile_order_on(long long tiles) { return tiles >= kOrderMinTiles; }
-
-// Key of a tile with list length len at offset pos of its XCD range of per
-// tiles: longest first, then by position window.
-__device__ __forceinline__ int order_key(int len, unsigned int pos, unsigned int per) {
-  const int lb = len < 256 ? len : min(kOrderLen - 1, 256 + ((len - 256) >> 3));
-  const int sub = (int)(((unsigned long long)pos * kOrderSub) / per);
-  return (kOrderLen - 1 - lb) * kOrderSub + sub;
-}
 
 // Workspace carve-up; every region starts on a 256-byte boundary.
 struct Layout {

@@ -617,24 +617,14 @@ struct RasterArgs {
   const int *order;
 };
 
-// Both rasters take their tiles longest list first (the binning's order),
-// except the 16-channel forward: each of its entries stages 64 bytes of
-// amplitudes, and frame-major dispatch keeps a frame's in L2 -- measured 4%
-// faster there, while its backward gains 6% from the order.
-template <int CP>
-struct ForwardOrdered {
-  static constexpr bool value = CP < 16;
-};
-
 template <int CP, int UW, int UX, int UY>
 void fwd_cp(const RasterArgs &a, hipStream_t st) {
   using WL = WaveLayout<UW, UX, UY>;
   dim3 grid((unsigned)xcd_grid(a.nT, a.B));
-  const int *order = ForwardOrdered<CP>::value ? a.order : nullptr;
   PDR_TIMED(PDR_K_FORWARD_RASTER, st,
             hipLaunchKernelGGL((k_forward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
                                a.recs, a.params, a.tile_off, a.list, a.B, a.N, a.H, a.W, a.C,
-                               a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr, order));
+                               a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr, a.order));
 }
 
 template <int CP, int UW, int UX, int UY>
