@@ -171,11 +171,17 @@ def test_workload_subset_parity(orc, idx, frames):
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
 def test_workload_full_size(orc, idx):
-    # full batch in the benchmark's launch configuration: lists bit-exact on
-    # every frame, image and gradients on sampled frames
+    # full batch in the benchmark's launch configuration: lists bit-exact and
+    # the image within tolerance on every frame (a tile the rasters' order
+    # skipped would leave its pixels unwritten; as the order has one slot
+    # per tile, a complete image also shows that the backward, which takes
+    # the same order, visits every tile once), gradients on sampled frames
     wl, p, g = workloads.make_inputs(idx)
     res = gpu_forward_backward(p, g, wl.H, wl.W)
     n = check_lists(orc, p, wl.H, wl.W)
+    ref, slk, _, _ = orc.render(p, wl.H, wl.W)
+    check_close(res["image"], ref, np.abs(ref), slk, "image, every frame")
+    del ref, slk
     frames = sorted({0, wl.B // 2, wl.B - 1})
     out = check_against_oracle(orc, p, g, wl.H, wl.W, frames=frames, gpu=res)
     print(wl.name, "pairs", n, out)
