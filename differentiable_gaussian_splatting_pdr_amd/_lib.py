@@ -60,6 +60,16 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
+        # One HIP runtime per process: PyTorch's ROCm wheel bundles its own
+        # libamdhip64 (loaded under a different file name), so if this library
+        # came first it would bind the system runtime and torch would load a
+        # second one beside it -- torch's streams and allocations would then
+        # be foreign handles to this library's launches.  With torch loaded
+        # first, this library's libamdhip64.so.7 resolves to torch's copy.
+        try:
+            import torch  # noqa: F401
+        except ImportError:   # a torch-free host (C ABI checks only)
+            pass
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 "libpdrsplat.so is not built (expected at %s); run "

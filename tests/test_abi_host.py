@@ -5,6 +5,7 @@ import math
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -216,3 +217,14 @@ def test_count_support_validates():
     assert L.pdr_splat_count_support(FAKE, 0, 4, 16, 16, 1, 3.0, FAKE, FAKE, 1 << 20, None) == -1
     assert L.pdr_splat_count_support(FAKE, 1, 4, 16, 16, 1, -1.0, FAKE, FAKE, 1 << 20, None) == -1
     assert L.pdr_splat_count_support(FAKE, 1, 4, 16, 16, 1, 3.0, FAKE, FAKE, 16, None) == -2
+
+
+def test_binding_loads_torch_first():
+    # the binding imports torch before loading the library (one HIP runtime
+    # per process): checked in a fresh interpreter that touches the library
+    # before anything else
+    code = ("import sys; from differentiable_gaussian_splatting_pdr_amd import _lib; "
+            "assert 'torch' not in sys.modules; _lib.lib(); assert 'torch' in sys.modules")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]

@@ -9,12 +9,14 @@
   with new parameter values and eager work in between, and every replay is
   checked against the eager result of the same values.
 """
+import os
+
 import numpy as np
 import pytest
 
 from differentiable_gaussian_splatting_pdr_amd import workloads
 
-from helpers import check_against_oracle
+from helpers import check_against_oracle, check_close
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +121,29 @@ def test_graph_capture_and_replay(orc):
         torch.cuda.synchronize()
         assert np.array_equal(got_img, img_e.cpu().numpy())
         check_against_oracle(orc, p, g, H, W, gpu={"image": got_img, "grad": got_gp})
+
+
+def test_library_loaded_before_torch(orc):
+    # a process that touches the binding before importing torch: the binding
+    # loads torch first, so the library shares torch's HIP runtime and its
+    # launches on torch's stream work (with two runtimes they fail)
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "from differentiable_gaussian_splatting_pdr_amd import _lib, workloads\n"
+        "_lib.pdr_splat_bin_variant(34, 108, 11, 92)\n"
+        "import numpy as np, torch\n"
+        "from differentiable_gaussian_splatting_pdr_amd import splat\n"
+        "p, _ = workloads.make_custom(34, 108, 11, 92, 2, seed=1000, s_range=(0.3, 9.0), mean_margin=6.0)\n"
+        "img, ws = splat.forward(torch.from_numpy(p).cuda(), 11, 92)\n"
+        "np.save(sys.argv[1], img.cpu().numpy())\n")
+    import tempfile
+    out = os.path.join(tempfile.mkdtemp(), "image.npy")
+    r = subprocess.run([sys.executable, "-c", "import sys\n" + code, out], cwd=root,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    p, _ = workloads.make_custom(34, 108, 11, 92, 2, seed=1000, s_range=(0.3, 9.0), mean_margin=6.0)
+    ref, slk, _, _ = orc.render(p, 11, 92)
+    check_close(np.load(out), ref, np.abs(ref), slk, "image from a process that loaded the library first")
+    os.remove(out)
