@@ -1,0 +1,58 @@
+"""Seeded random shapes through the whole path, on the GPU.
+
+Each case draws a batch size, a Gaussian count, a ragged frame size and a
+channel count from a fixed seed, spanning the binning variants (consecutive,
+member, column chunks, two-level) and the rasters' tile order (on from 1024
+tiles), and checks: tile lists bit-exact against the oracle, the image and
+the gradients (tile and, where it applies, span backward) within the
+tolerance of ``helpers``.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from differentiable_gaussian_splatting_pdr_amd import workloads
+
+from helpers import check_against_oracle, check_lists, gpu_forward_backward
+
+pytestmark = pytest.mark.gpu
+
+
+def _shape(k, rng):
+    kind = k % 4
+    if kind == 0:     # small batches of small frames
+        return (int(rng.integers(1, 40)), int(rng.integers(1, 600)), int(rng.integers(8, 140)),
+                int(rng.integers(8, 140)))
+    if kind == 1:     # many frames: the tile order is on
+        return (int(rng.integers(40, 120)), int(rng.integers(50, 400)), int(rng.integers(40, 90)),
+                int(rng.integers(40, 90)))
+    if kind == 2:     # wide single frames: column chunks
+        return (1, int(rng.integers(1000, 12000)), int(rng.integers(16, 200)),
+                int(rng.integers(1000, 6000)))
+    return (int(rng.integers(1, 4)), int(rng.integers(16384, 30000)), int(rng.integers(200, 600)),
+            int(rng.integers(200, 600)))  # two-level
+
+
+CASES = []
+_rng = np.random.default_rng(4242)
+for _k in range(12):
+    CASES.append(_shape(_k, _rng) + (int(_rng.integers(1, 6)),))
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dN%d_%dx%dx%d" % c)
+def test_random_shapes(orc, case):
+    from differentiable_gaussian_splatting_pdr_amd import _lib
+    B, N, H, W, C = case
+    p, g = workloads.make_custom(B, N, H, W, C, seed=sum(case), s_range=(0.3, 9.0),
+                                 mean_margin=6.0)
+    n = check_lists(orc, p, H, W)
+    out = check_against_oracle(orc, p, g, H, W)
+    try:
+        res = gpu_forward_backward(p, g, H, W, algo=_lib.PDR_BWD_SPAN)
+        check_against_oracle(orc, p, g, H, W, gpu=res)
+        span = "span ok"
+    except _lib.PdrError:
+        span = "span n/a"
+    print(case, "variant", _lib.pdr_splat_bin_variant(B, N, H, W), "tiles",
+          B * math.ceil(H / 16) * math.ceil(W / 16), "pairs", n, out, span)
