@@ -722,15 +722,15 @@ static bool member_rule(int N, const BinGroups &bg) {
 }
 
 // Second level of the two-level binning: one tile row per group, cut into
-// column chunks so that the grid has about kBinTargetGroups workgroups (a
+// column chunks so that the grid has about kBinRowTargetGroups workgroups (a
 // chunk scans only its row's list, so chunks cost no rescans of the frame).
 static BinGroups row_groups(int B, int N, int nTx, int nTy) {
   BinGroups r;
   r.gh = 1;
   const long long rows_all = (long long)B * nTy;
   int c = 1;
-  if (rows_all < kBinTargetGroups && nTx >= 2 * kBinMinChunkTiles) {
-    c = (int)((kBinTargetGroups + rows_all - 1) / rows_all);
+  if (rows_all < kBinRowTargetGroups && nTx >= 2 * kBinMinChunkTiles) {
+    c = (int)((kBinRowTargetGroups + rows_all - 1) / rows_all);
     if (c > nTx / kBinMinChunkTiles) c = nTx / kBinMinChunkTiles;
   }
   r.cw = (nTx + c - 1) / c;

@@ -23,6 +23,10 @@ constexpr long long kMaxChunk = 4096;   // Gaussians per binning chunk (bit-matr
 #define PDR_BIN_TARGET_GROUPS 2048
 #endif
 constexpr long long kBinTargetGroups = PDR_BIN_TARGET_GROUPS;  // binning workgroups to aim for
+// ... for the second level of two-level binning, whose groups are column
+// chunks of one tile row: measured on one 2048x2048 frame, 98 us of binning
+// at 1024 groups against 136 us at 2048 (wider chunks)
+constexpr long long kBinRowTargetGroups = 1024;
 constexpr long long kBinLdsBytes = 60 * 1024 - 512;  // + 4.2 KB of static arrays stays within 64 KB
 #ifndef PDR_BIN_MEMBERS
 #define PDR_BIN_MEMBERS -1
