@@ -26,9 +26,10 @@
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers (hipMalloc / torch), fp32 or
- *    int32, C-contiguous, owned by the caller.  The library never allocates
- *    or frees device memory; everything it needs lives in the caller's
- *    workspace.
+ *    int32 (one uint64 for pdr_splat_count_support; fp16 / bf16 images for
+ *    the _fmt variants), C-contiguous, owned by the caller.  The library
+ *    never allocates or frees device memory; everything it needs lives in
+ *    the caller's workspace (256-byte aligned).
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
  *    enqueue work and return without synchronising, except pdr_splat_check.
  *  - Arguments are validated before anything is enqueued; a negative status
