@@ -159,6 +159,24 @@ def test_forward_is_deterministic():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("idx", [2, 4])
+def test_forward_is_deterministic_with_the_tile_order(idx):
+    # at full size the rasters take the binning's longest-first tile order
+    # (built with atomics, so its slots within a key vary from run to run):
+    # repeated forwards on one workspace and on fresh ones give the same bits
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import _lib, splat
+    wl, p, _ = workloads.make_inputs(idx, with_grad=False)
+    T = _lib.pdr_splat_tile_size()
+    assert wl.B * -(-wl.H // T) * -(-wl.W // T) >= 1024   # the order is on
+    pt = torch.from_numpy(p).cuda()
+    ref, ws = splat.forward(pt, wl.H, wl.W)
+    ref = ref.clone()
+    for k in range(4):
+        img, _ = splat.forward(pt, wl.H, wl.W, workspace=ws if k % 2 else None)
+        assert torch.equal(img, ref), k
+
+
 # --- the five workloads ---------------------------------------------------------
 
 @pytest.mark.parametrize("idx,frames", [(0, None), (1, 12), (2, 4), (3, 2), (4, 1)])
