@@ -433,6 +433,11 @@ def main():
         "frames_per_s": B / (ms * 1e-3),
         "support_pairs": support_pairs,
         "tile_pairs": int(tile_pairs),
+        # every listed (tile, Gaussian) entry spans T*T pixel lanes; the
+        # support pairs among them show the lane waste before unit culling
+        "tile_lane_pairs": int(tile_pairs) * T * T,
+        "tile_lane_efficiency": (round(support_pairs / (int(tile_pairs) * T * T), 4)
+                                 if support_pairs and tile_pairs else None),
         "fp32_peak_frac_fwd_bwd": (round(support_pairs * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
                                          / FP32_PEAK_TFLOPS, 4) if support_pairs else None),
         "ms_per_step_host": round(host_ms, 5),

@@ -43,6 +43,9 @@ def test_bench_line():
     assert d["value"] > 0 and d["ms_per_step"] > 0
     assert abs(d["value"] - d["support_pairs"] / (d["ms_per_step"] * 1e-3)) <= 1e-4 * d["value"]
 
+    assert d["tile_lane_pairs"] == 256 * d["tile_pairs"]
+    assert 0 < d["tile_lane_efficiency"] <= 1
+
     rl = d["roofline"]
     assert rl["bound"] in ("hbm", "mfma", "alu")
     assert rl["unit"] in ("GB/s", "TFLOP/s")
