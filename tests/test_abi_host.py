@@ -228,3 +228,32 @@ def test_binding_loads_torch_first():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_no_fallback_without_the_library():
+    """The bindings only marshal arguments: with the library missing every
+    call raises, and rendering a CPU tensor raises instead of computing
+    (there is no CPU path).  Run in a child process so that this process's
+    loaded library is untouched."""
+    code = r'''
+import torch
+from differentiable_gaussian_splatting_pdr_amd import _lib, splat
+_lib.LIB_PATH = "/nonexistent/libpdrsplat.so"
+_lib._lib = None
+try:
+    _lib.pdr_splat_tile_size()
+except RuntimeError as e:
+    assert "not built" in str(e), e
+else:
+    raise SystemExit("binding ran without the library")
+try:
+    splat.render(torch.zeros(1, 4, 8), 16, 16)
+except Exception as e:
+    print("render raised", type(e).__name__)
+else:
+    raise SystemExit("render produced an image without the library")
+'''
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "render raised" in r.stdout
