@@ -403,7 +403,7 @@ def main():
         avg = kernels[dom]["avg_ms"] * 1e-3
         ach = fl / avg / 1e12
         traffic = None
-        tpath = os.path.join(ROOT, "profiles", "traffic_%s_cfg%d.json" % (dom, args.workload))
+        tpath = os.path.join(ROOT, "profiles", "traffic_%s_%dx%dx%dx%d_n%d.json" % (dom, B, H, W, C, N))
         if os.path.exists(tpath):
             with open(tpath) as fh:
                 t = json.load(fh)
