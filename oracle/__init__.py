@@ -9,10 +9,10 @@ only builds it with gcc and marshals numpy arrays through ctypes.  What each
 function computes, and from which passage of the pages, is stated in the C
 file's header:
 
-* ``render``  -- I[b,y,x,c] = sum_n a w, with per-pixel slack (truncation
-  ties, plus with ``cond`` the single-precision allowance of each pair) and
-  magnitude (sum of |terms|); ``allpairs=True`` evaluates every (pixel,
-  Gaussian) pair with no pruning.
+* ``render``  -- I[b,y,x,c] = sum_n a w, with per-pixel slack (the terms of
+  pairs within the truncation-tie band |q - k^2| <= tau k^2) and magnitude
+  (sum of |terms|); ``allpairs=True`` evaluates every (pixel, Gaussian) pair
+  with no pruning.
 * ``grad``    -- the analytic backward dL/d(mu, s, theta, a) with slack and
   magnitude per output.
 * ``count_support`` -- per frame, the number of (Gaussian, pixel) pairs
@@ -58,9 +58,9 @@ def _load():
         ip = ctypes.POINTER(ctypes.c_int)
         lp = ctypes.POINTER(ctypes.c_longlong)
         i, d = ctypes.c_int, ctypes.c_double
-        lib.orc_render.argtypes = [dp, i, i, i, i, i, d, d, i, i, i, dp, dp, dp, lp]
+        lib.orc_render.argtypes = [dp, i, i, i, i, i, d, d, i, i, dp, dp, dp, lp]
         lib.orc_render.restype = ctypes.c_int
-        lib.orc_grad.argtypes = [dp, dp, i, i, i, i, i, d, d, i, i, dp, dp, dp]
+        lib.orc_grad.argtypes = [dp, dp, i, i, i, i, i, d, d, i, dp, dp, dp]
         lib.orc_grad.restype = ctypes.c_int
         lib.orc_bin.argtypes = [dp, i, i, i, i, i, d, i, i, ip, lp, ip, ctypes.c_longlong, ip]
         lib.orc_bin.restype = ctypes.c_longlong
@@ -88,12 +88,10 @@ def _params64(params):
     return p
 
 
-def render(params, H, W, radius=3.0, tau=TAU, allpairs=False, nthreads=None, extras=True,
-           cond=True):
+def render(params, H, W, radius=3.0, tau=TAU, allpairs=False, nthreads=None, extras=True):
     """Return (image, slack, mag, pairs) as fp64 [B,H,W,C] (+ int64 [B]).
 
-    slack holds the truncation-tie terms and, with ``cond``, the
-    single-precision allowance of every pair (oracle.c header)."""
+    slack holds the |terms| of the pairs in the truncation-tie band."""
     p = _params64(params)
     B, N, P = p.shape
     C = P - 5
@@ -102,7 +100,7 @@ def render(params, H, W, radius=3.0, tau=TAU, allpairs=False, nthreads=None, ext
     mag = np.empty_like(img) if extras else None
     pairs = np.zeros(B, np.int64)
     rc = _load().orc_render(_ptr(p, ctypes.c_double), B, N, H, W, C, float(radius), float(tau),
-                            int(bool(cond)), int(bool(allpairs)), int(nthreads or default_threads()),
+                            int(bool(allpairs)), int(nthreads or default_threads()),
                             _ptr(img, ctypes.c_double), _ptr(slk, ctypes.c_double),
                             _ptr(mag, ctypes.c_double), _ptr(pairs, ctypes.c_longlong))
     if rc != 0:
@@ -110,7 +108,7 @@ def render(params, H, W, radius=3.0, tau=TAU, allpairs=False, nthreads=None, ext
     return img, slk, mag, pairs
 
 
-def grad(params, grad_image, H, W, radius=3.0, tau=TAU, nthreads=None, extras=True, cond=True):
+def grad(params, grad_image, H, W, radius=3.0, tau=TAU, nthreads=None, extras=True):
     """Return (grad, slack, mag) as fp64 [B,N,5+C] (slack as in ``render``)."""
     p = _params64(params)
     B, N, P = p.shape
@@ -122,8 +120,8 @@ def grad(params, grad_image, H, W, radius=3.0, tau=TAU, nthreads=None, extras=Tr
     slk = np.empty_like(p) if extras else None
     mag = np.empty_like(p) if extras else None
     rc = _load().orc_grad(_ptr(p, ctypes.c_double), _ptr(g, ctypes.c_double), B, N, H, W, C,
-                          float(radius), float(tau), int(bool(cond)),
-                          int(nthreads or default_threads()), _ptr(out, ctypes.c_double), _ptr(slk, ctypes.c_double),
+                          float(radius), float(tau), int(nthreads or default_threads()),
+                          _ptr(out, ctypes.c_double), _ptr(slk, ctypes.c_double),
                           _ptr(mag, ctypes.c_double))
     if rc != 0:
         raise ValueError("orc_grad failed: %d" % rc)
