@@ -1,7 +1,8 @@
 // bin.hip -- per-Gaussian preprocessing and tile binning.
 //
 //  k_preprocess   one thread per Gaussian: validity, fp64 pixel bounding box
-//                 of the truncated ellipse q <= k^2, whitening rows.
+//                 of the truncated ellipse q <= k^2, whitening rows (and the
+//                 compensation constants of thin Gaussians).
 //  k_bin<false,M,X> per (frame, tile group): per-tile overlap counts.
 //  k_bin<true,M,X>  per (frame, tile group): the per-tile lists, ascending
 //                   Gaussian index, at the scanned offsets.
@@ -57,6 +58,7 @@ constexpr int kZeroBlocks = 32;   // preprocess blocks at least (for clearing th
 __global__ __launch_bounds__(256) void k_preprocess(const float *__restrict__ params, int BN, int C,
                                                     FastDiv pdiv, int H, int W, float radius,
                                                     GRec *__restrict__ recs,
+                                                    ThinRec *__restrict__ thin,
                                                     uint2 *__restrict__ boxes, WsHeader *hdr,
                                                     int stamp_N, unsigned long long stamp_ptr,
                                                     int *__restrict__ ohist) {
@@ -105,19 +107,22 @@ __global__ __launch_bounds__(256) void k_preprocess(const float *__restrict__ pa
   r.bx = kEmptyBox;
   r.by = kEmptyBox;
   if (ok) {
-    double sn, cs;
-    sincos((double)th, &sn, &cs);
+    double L[4], sn, cs;
+    whitening_rows(th, s1, s2, L, &sn, &cs);
     int b[4];
     pixel_box(mx, my, s1, s2, cs, sn, (double)radius, H, W, b);
     if (b[0] <= b[1] && b[2] <= b[3]) {
       r.bx = (unsigned)b[0] | ((unsigned)b[1] << 16);
       r.by = (unsigned)b[2] | ((unsigned)b[3] << 16);
     }
-    double i1 = kKappa / (double)s1, i2 = kKappa / (double)s2;
-    r.l11 = clamp_to_float(cs * i1);
-    r.l12 = clamp_to_float(sn * i1);
-    r.l21 = clamp_to_float(-sn * i2);
-    r.l22 = clamp_to_float(cs * i2);
+    r.l11 = clamp_to_float(L[0]);
+    r.l12 = clamp_to_float(L[1]);
+    r.l21 = clamp_to_float(L[2]);
+    r.l22 = clamp_to_float(L[3]);
+    if (is_thin(r.l11, r.l12, r.l21, r.l22)) {
+      const float l32[4] = {r.l11, r.l12, r.l21, r.l22};
+      thin[i] = make_thin_rec(mx, my, L, l32);
+    }
   }
   recs[i] = r;
   boxes[i] = make_uint2(r.bx, r.by);
@@ -811,7 +816,7 @@ hipError_t launch_preprocess(const float *params, int B, int N, int H, int W, in
   PDR_TIMED(PDR_K_PREPROCESS, st,
             hipLaunchKernelGGL(k_preprocess, dim3((unsigned)blocks), dim3(256), 0, st,
                                params, (int)BN, C, make_fastdiv((uint32_t)(5 + C)), H, W, radius,
-                               (GRec *)(w + L.recs),
+                               (GRec *)(w + L.recs), (ThinRec *)(w + L.thin),
                                (uint2 *)(w + L.boxes), (WsHeader *)(w + L.hdr), N,
                                stamp_valid ? (unsigned long long)(uintptr_t)params : 0ull,
                                ordered ? (int *)(w + L.ohist) : (int *)nullptr));

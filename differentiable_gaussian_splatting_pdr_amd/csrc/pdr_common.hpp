@@ -26,6 +26,118 @@ constexpr int kMaxN = 1 << 22;   // per-frame Gaussian count bound of the scan's
 constexpr double kKappa = 0.84932180028801904272150283410289;
 constexpr double kKappa2 = 0.72134752044448170367996234050095;  // log2(e) / 2
 
+// The whitening rows in fp64, scaled by kappa: [[c/s1, s/s1], [-s/s2, c/s2]]
+// (c, s = cos, sin of theta, also returned).  Preprocessing rounds them to
+// fp32 for the per-Gaussian records; the compensated evaluation of thin
+// Gaussians recomputes them with the same expressions to recover the
+// rounding residues.
+__device__ __forceinline__ void whitening_rows(float th, float s1, float s2, double *L, double *sn,
+                                               double *cs) {
+  sincos((double)th, sn, cs);
+  const double i1 = kKappa / (double)s1, i2 = kKappa / (double)s2;
+  L[0] = *cs * i1;
+  L[1] = *sn * i1;
+  L[2] = -*sn * i2;
+  L[3] = *cs * i2;
+}
+
+// Thin Gaussians.  In single precision z = L (p - mu) carries an absolute
+// error of order u |L| |p - mu|, and for a Gaussian of anisotropy R the thin
+// axis's |L| |p - mu| reaches R k on its support: for R beyond about 10 the
+// thin coordinate's error, which rounding of L makes systematic across the
+// pixels, moves the theta and thin-scale gradients by more than 1e-4 of
+// their value (measured: none above tolerance up to 10:1, some from 12:1).
+// Gaussians with row norms |L_2|^2 > 64 |L_1|^2 (anisotropy above 8:1) are
+// evaluated with compensation instead:
+//  * the mean is split as mu = mh + r with mh a multiple of 2^-8 and
+//    |r| <= 2^-9, so p - (mh - o) is exact in fp32 for any pixel centre p
+//    relative to an integer origin o while |p - mh + o| < 2^16, and r is
+//    folded into a constant per row, c_i = -L_i r (fp64, rounded);
+//  * the rows are ordered so that row 2 is the thin one (swapped: the sums
+//    of the two rows trade places);
+//  * row 2 is evaluated as a float pair: the fp32 row (hi), its fp64
+//    rounding residue (lo), and the exact product residue of l22 dy, so its
+//    error is u |z2| + O(u^2 |L| |p - mu|).
+// Preprocessing writes these constants for every thin Gaussian into a
+// per-Gaussian side record; the rasters take them at staging.
+constexpr float kThinRatio2 = 64.f;
+// The forward image (and the support count, which follows the forward) meets
+// its bound with the plain evaluation far beyond that: its terms are the
+// weights themselves, whose relative error stays near u R k, and its
+// truncation test keeps that error well inside the tie band up to about
+// 100:1.  The rasters' forward takes the compensation above 32:1 only.
+constexpr float kThinRatio2Fwd = 1024.f;
+constexpr double kThinQuantum = 256.0;
+constexpr double kThinMaxMean = 16376.0;   // |mh| bound: |p - mh + o| < 2^16 for o, p < 2^15
+constexpr int kThinOk = 1, kThinSwap = 2;
+struct __attribute__((aligned(16))) ThinRec {
+  float mhx, mhy;     // split mean (multiples of 2^-8)
+  float lo21, lo22;   // fp64 residues of the thin row
+  float c1, c2;       // -L_i r
+  int flags;          // kThinOk | kThinSwap
+  int pad;
+};
+static_assert(sizeof(ThinRec) == 32, "thin record is 32 bytes");
+// The per-entry part the rasters keep in LDS.
+struct ThinX {
+  float lo21, lo22, c1, c2;
+};
+
+__device__ __forceinline__ bool is_thin(float l11, float l12, float l21, float l22,
+                                        float ratio2 = kThinRatio2) {
+  const float n1 = l11 * l11 + l12 * l12, n2 = l21 * l21 + l22 * l22;
+  const float lo = fminf(n1, n2), hi = fmaxf(n1, n2);
+  return hi > ratio2 * lo && hi < 1e30f;
+}
+
+// The thin record of a Gaussian with mean (mx, my), fp64 rows L and their
+// fp32 roundings l (record order).
+__device__ __forceinline__ ThinRec make_thin_rec(float mx, float my, const double *L64,
+                                                 const float *l32) {
+  ThinRec t{};
+  const double hx = rint((double)mx * kThinQuantum) / kThinQuantum;
+  const double hy = rint((double)my * kThinQuantum) / kThinQuantum;
+  if (!(fabs(hx) <= kThinMaxMean && fabs(hy) <= kThinMaxMean)) return t;   // flags 0: plain
+  double L[4] = {L64[0], L64[1], L64[2], L64[3]};
+  float l[4] = {l32[0], l32[1], l32[2], l32[3]};
+  const bool sw = l[0] * l[0] + l[1] * l[1] > l[2] * l[2] + l[3] * l[3];
+  if (sw) {
+    double d = L[0]; L[0] = L[2]; L[2] = d;
+    d = L[1]; L[1] = L[3]; L[3] = d;
+    float f = l[0]; l[0] = l[2]; l[2] = f;
+    f = l[1]; l[1] = l[3]; l[3] = f;
+  }
+  const double rx = (double)mx - hx, ry = (double)my - hy;  // exact, |r| <= 2^-9
+  t.mhx = (float)hx;
+  t.mhy = (float)hy;
+  t.lo21 = (float)(L[2] - (double)l[2]);
+  t.lo22 = (float)(L[3] - (double)l[3]);
+  t.c1 = (float)(-(L[0] * rx + L[1] * ry));
+  t.c2 = (float)(-(L[2] * rx + L[3] * ry));
+  t.flags = kThinOk | (sw ? kThinSwap : 0);
+  return t;
+}
+
+// z' = L (p - mu) of one pixel from d = p - mu (plain), or for a thin
+// Gaussian from d = p - mh (exact) with the compensation constants.
+template <bool THIN>
+__device__ __forceinline__ void whiten(float l11, float l12, float l21, float l22, const ThinX &tx,
+                                       float dx, float dy, float &u1, float &u2) {
+  if constexpr (THIN) {
+    u1 = fmaf(l11, dx, fmaf(l12, dy, tx.c1));
+    const float p = l22 * dy;
+    const float e = fmaf(l22, dy, -p);  // l22 dy - p, exactly
+    const float s = fmaf(l21, dx, p);   // one rounding, relative to the result
+    float t = e + tx.c2;
+    t = fmaf(tx.lo22, dy, t);
+    t = fmaf(tx.lo21, dx, t);
+    u2 = s + t;
+  } else {
+    u1 = l11 * dx + l12 * dy;
+    u2 = l21 * dx + l22 * dy;
+  }
+}
+
 // Status bits raised on the device into the workspace header.
 constexpr int kStatusOverflow = 1;
 constexpr int kStatusStale = 2;
@@ -36,7 +148,8 @@ struct WsHeader {
   long long total;   // (tile, Gaussian) pairs of the last binning
   long long cap;     // list capacity used by the last binning
   int stamp[8];      // B, N, H, W, C, radius bits, params pointer lo/hi at binning
-  int pad1[50];
+  int nonfinite;     // the last tile backward met a non-finite dL/dI value
+  int pad1[49];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
 
@@ -92,7 +205,7 @@ inline bool tile_order_on(long long tiles) { return tiles >= kOrderMinTiles; }
 
 // Workspace carve-up; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t hdr, recs, boxes, counts, gtot, tile_off, order, ohist, list, total;
+  size_t hdr, recs, thin, boxes, counts, gtot, tile_off, order, ohist, list, total;
   size_t rcnt, fstart, rlist;   // per-row member lists (two-level binning only)
   long long cap;
 };
@@ -139,6 +252,7 @@ inline Layout make_layout(long long BN, long long BT, long long cap, const RowPl
   size_t o = 0;
   L.hdr = o;       o += align256(sizeof(WsHeader));
   L.recs = o;      o += align256(size_t(BN) * sizeof(GRec));
+  L.thin = o;      o += align256(size_t(BN) * sizeof(ThinRec));
   L.boxes = o;     o += align256(size_t(BN) * 8);
   L.counts = o;    o += align256(size_t(BT) * 4);
   L.gtot = o;      o += align256(size_t(BT) * 4);

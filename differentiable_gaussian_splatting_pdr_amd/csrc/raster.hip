@@ -36,6 +36,9 @@
 
 namespace pdr {
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
 template <int UW, int UX, int UY>
 struct WaveLayout {
   static constexpr int kUH = kWave / UW;
@@ -91,21 +94,36 @@ __device__ __forceinline__ bool unit_missed(const EllipseRows &E, float X0, floa
   return qmin > thr + 1e-4f * (thr + E.r2 * dm * dm);
 }
 
-// One list entry per thread of the workgroup (computed here, in parallel,
-// so that the per-entry loop only reads and tests bits).  The unit mask
-// holds the units the pixel box meets, less those the truncated ellipse
-// misses.
-template <int CP, int UW>
-__device__ __forceinline__ void stage_entry(Entry<CP> *s, const GRec *__restrict__ recs,
-                                            const float *__restrict__ params,
-                                            const int *__restrict__ list, int s0, int cnt,
-                                            size_t gbase, int P, int c0, int cc, int tid,
-                                            int tx0, int ty0, float thr) {
+// Flag above the unit bits of a thin entry's mask: its rows were swapped
+// for the compensated evaluation (the sums of the two rows trade places).
+constexpr unsigned int kEntrySwap = 0x40000000u;
+
+// Stages the list entries [s0, s0 + cnt) of the tile, one per thread of the
+// workgroup (computed here, in parallel, so that the per-entry loop only
+// reads and tests bits).  The unit mask holds the units the pixel box meets,
+// less those the truncated ellipse misses.  A thin Gaussian's entry gets the
+// split tile-local mean, its rows in thin-row-last order and, in sx at the
+// same slot, the compensation constants (the forward rasters, FWD, take it
+// above a higher anisotropy than the backward).  Plain entries are written first
+// and thin ones after them, each group in list order, so that the rasters
+// run one loop per evaluation with no per-entry branch between them; the
+// number of plain entries is returned (wave-uniform).  scnt: 2 * WAVES
+// ints of LDS (used with more than one wave).
+template <int CP, int UW, int WAVES, bool FWD>
+__device__ __forceinline__ int stage_batch(Entry<CP> *s, ThinX *sx, int *scnt,
+                                           const GRec *__restrict__ recs,
+                                           const ThinRec *__restrict__ thin,
+                                           const float *__restrict__ params,
+                                           const int *__restrict__ list, int s0, int cnt,
+                                           size_t gbase, int P, int c0, int cc, int tid, int tx0,
+                                           int ty0, float thr) {
   constexpr int UH = kWave / UW, NUX = kTileW / UW, NUY = kTileH / UH;
+  Entry<CP> e;
+  ThinX tx{};
+  bool is_thin_entry = false;
   if (tid < cnt) {
     const int n = list[s0 + tid];
     const GRec r = recs[gbase + n];
-    Entry<CP> e;
     e.l11 = r.l11;
     e.l12 = r.l12;
     e.l21 = r.l21;
@@ -142,9 +160,66 @@ __device__ __forceinline__ void stage_entry(Entry<CP> *s, const GRec *__restrict
       if (unit_missed(E, X0, X0 + (float)(UW - 1), Y0, Y0 + (float)(UH - 1), thr))
         m &= ~(1u << u);
     }
+    if (is_thin(e.l11, e.l12, e.l21, e.l22, FWD ? kThinRatio2Fwd : kThinRatio2)) {
+      const ThinRec tr = thin[gbase + n];
+      if (tr.flags & kThinOk) {
+        is_thin_entry = true;
+        if (tr.flags & kThinSwap) {
+          float f = e.l11; e.l11 = e.l21; e.l21 = f;
+          f = e.l12; e.l12 = e.l22; e.l22 = f;
+          m |= kEntrySwap;
+        }
+        e.mx = tr.mhx - (float)tx0;   // exact: multiples of 2^-8 below 2^16
+        e.my = tr.mhy - (float)ty0;
+        tx = ThinX{tr.lo21, tr.lo22, tr.c1, tr.c2};
+      }
+    }
     e.mask = m;
-    s[tid] = e;
   }
+  // slots: plain entries first, then thin ones, list order within each
+  const unsigned long long tb = __builtin_amdgcn_ballot_w64(tid < cnt && is_thin_entry);
+  const unsigned long long pb = __builtin_amdgcn_ballot_w64(tid < cnt && !is_thin_entry);
+  const int below_t = __builtin_amdgcn_mbcnt_hi((unsigned)(tb >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((unsigned)tb, 0u));
+  const int below_p = __builtin_amdgcn_mbcnt_hi((unsigned)(pb >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((unsigned)pb, 0u));
+  int nplain, pos;
+  if constexpr (WAVES == 1) {
+    nplain = __popcll(pb);
+    pos = is_thin_entry ? nplain + below_t : below_p;
+  } else {
+    const int wave = tid >> 6;
+    if ((tid & 63) == 0) {
+      scnt[wave] = __popcll(pb);
+      scnt[WAVES + wave] = __popcll(tb);
+    }
+    __syncthreads();
+    int pbefore = 0, tbefore = 0;
+    nplain = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      pbefore += w < wave ? scnt[w] : 0;
+      tbefore += w < wave ? scnt[WAVES + w] : 0;
+      nplain += scnt[w];
+    }
+    pos = is_thin_entry ? nplain + tbefore + below_t : pbefore + below_p;
+    nplain = __builtin_amdgcn_readfirstlane(nplain);
+  }
+  if (tid < cnt) {
+    s[pos] = e;
+    if (is_thin_entry) sx[pos] = tx;
+  }
+  return nplain;
+}
+
+// The compensation constants of an entry in scalar registers (they are
+// wave-uniform; the thin loops then hold no more vector registers than the
+// plain ones).
+__device__ __forceinline__ float sgpr(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+__device__ __forceinline__ ThinX uniform(const ThinX &t) {
+  return ThinX{sgpr(t.lo21), sgpr(t.lo22), sgpr(t.c1), sgpr(t.c2)};
 }
 
 // Where the image (forward output, backward input) lives: value (pixel, c)
@@ -179,9 +254,10 @@ __device__ __forceinline__ float load_image(const void *base, size_t idx, int fm
 
 template <int CP, int UW, int UX, int UY>
 __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
-    const GRec *__restrict__ recs, const float *__restrict__ params,
-    const int *__restrict__ tile_off, const int *__restrict__ list, int B, int N, int H, int W,
-    int C, int c0, int cc, float thr, int nTx, int nT, void *__restrict__ image, ImgView iv,
+    const GRec *__restrict__ recs, const ThinRec *__restrict__ thin,
+    const float *__restrict__ params, const int *__restrict__ tile_off,
+    const int *__restrict__ list, int B, int N, int H, int W, int C, int c0, int cc, float thr,
+    int nTx, int nT, void *__restrict__ image, ImgView iv,
     const WsHeader *hdr, const int *__restrict__ order) {
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
@@ -191,6 +267,8 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
             : !xcd_frame_item(blockIdx.x, nT, B, &f, &t))
     return;
   __shared__ Entry<CP> s[WL::kBatch];
+  __shared__ ThinX sx[WL::kBatch];
+  __shared__ int scnt[2 * WL::kWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int tx0 = (t % nTx) * kTileW, ty0 = (t / nTx) * kTileH;
@@ -214,36 +292,44 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
-    stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0, thr);
+    const int np = stage_batch<CP, UW, WL::kWaves, true>(s, sx, scnt, recs, thin, params, list, s0, cnt,
+                                                   gbase, P, c0, cc, tid, tx0, ty0, thr);
     __syncthreads();
-    // the entry loop runs on a scalar count; each entry is read whole (its
-    // unit mask is all but never empty for a listed Gaussian)
-    const int ecnt = __builtin_amdgcn_readfirstlane(cnt);
-    for (int e = 0; e < ecnt; ++e) {
-      const Entry<CP> r = s[e];
-      const unsigned int um =
-          (__builtin_amdgcn_readfirstlane(r.mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
-      if (um == 0u) continue;
-      float a[CP];
+    // the entry loops run on scalar counts; each entry is read whole (its
+    // unit mask is all but never empty for a listed Gaussian).  THIN: the
+    // compensated evaluation of the batch's thin entries, after the others.
+    auto run = [&](auto thinc, int e0, int e1) {
+      constexpr bool THIN = decltype(thinc)::value != 0;
+      for (int e = e0; e < e1; ++e) {
+        const Entry<CP> r = s[e];
+        const unsigned int um =
+            (__builtin_amdgcn_readfirstlane(r.mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+        if (um == 0u) continue;
+        ThinX tx{};
+        if constexpr (THIN) tx = uniform(sx[e]);
+        float a[CP];
 #pragma unroll
-      for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
+        for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
 #pragma unroll
-      for (int j = 0; j < UY; ++j) {
-        if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
-        const float dy = (fy + (float)(UH * j)) - r.my;
+        for (int j = 0; j < UY; ++j) {
+          if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
+          const float dy = (fy + (float)(UH * j)) - r.my;
 #pragma unroll
-        for (int i = 0; i < UX; ++i) {
-          if (!(um & (1u << (j * UX + i)))) continue;
-          const float dx = (fx + (float)(UW * i)) - r.mx;
-          const float u1 = r.l11 * dx + r.l12 * dy;
-          const float u2 = r.l21 * dx + r.l22 * dy;
-          const float q = u1 * u1 + u2 * u2;
-          const float w = q <= thr ? __builtin_amdgcn_exp2f(-q) : 0.f;
+          for (int i = 0; i < UX; ++i) {
+            if (!(um & (1u << (j * UX + i)))) continue;
+            const float dx = (fx + (float)(UW * i)) - r.mx;
+            float u1, u2;
+            whiten<THIN>(r.l11, r.l12, r.l21, r.l22, tx, dx, dy, u1, u2);
+            const float q = u1 * u1 + u2 * u2;
+            const float w = q <= thr ? __builtin_amdgcn_exp2f(-q) : 0.f;
 #pragma unroll
-          for (int c = 0; c < CP; ++c) acc[j][i][c] += a[c] * w;
+            for (int c = 0; c < CP; ++c) acc[j][i][c] += a[c] * w;
+          }
         }
       }
-    }
+    };
+    run(IC<0>{}, 0, np);
+    run(IC<1>{}, np, __builtin_amdgcn_readfirstlane(cnt));
   }
 #pragma unroll
   for (int j = 0; j < UY; ++j) {
@@ -275,9 +361,10 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
 // figures.
 template <int UW, int UX, int UY>
 __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_count_support(
-    const GRec *__restrict__ recs, const float *__restrict__ params,
-    const int *__restrict__ tile_off, const int *__restrict__ list, int B, int N, int H, int W,
-    int C, float thr, int nTx, int nT, unsigned long long *__restrict__ count,
+    const GRec *__restrict__ recs, const ThinRec *__restrict__ thin,
+    const float *__restrict__ params, const int *__restrict__ tile_off,
+    const int *__restrict__ list, int B, int N, int H, int W, int C, float thr, int nTx, int nT,
+    unsigned long long *__restrict__ count,
     const WsHeader *hdr) {
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
@@ -285,6 +372,8 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_count_su
   if (!xcd_frame_item(blockIdx.x, nT, B, &f, &t)) return;
   if (hdr->status & kStatusOverflow) return;
   __shared__ Entry<1> s[WL::kBatch];
+  __shared__ ThinX sx[WL::kBatch];
+  __shared__ int scnt[2 * WL::kWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tx0 = (t % nTx) * kTileW, ty0 = (t / nTx) * kTileH;
@@ -300,31 +389,38 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_count_su
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
-    stage_entry<1, UW>(s, recs, params, list, s0, cnt, gbase, P, 0, 1, tid, tx0, ty0, thr);
+    const int np = stage_batch<1, UW, WL::kWaves, true>(s, sx, scnt, recs, thin, params, list, s0, cnt,
+                                                  gbase, P, 0, 1, tid, tx0, ty0, thr);
     __syncthreads();
-    const int ecnt = __builtin_amdgcn_readfirstlane(cnt);
-    for (int e = 0; e < ecnt; ++e) {
-      const Entry<1> r = s[e];
-      const unsigned int um =
-          (__builtin_amdgcn_readfirstlane(r.mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
-      if (um == 0u) continue;
+    auto run = [&](auto thinc, int e0, int e1) {
+      constexpr bool THIN = decltype(thinc)::value != 0;
+      for (int e = e0; e < e1; ++e) {
+        const Entry<1> r = s[e];
+        const unsigned int um =
+            (__builtin_amdgcn_readfirstlane(r.mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+        if (um == 0u) continue;
+        ThinX tx{};
+        if constexpr (THIN) tx = uniform(sx[e]);
 #pragma unroll
-      for (int j = 0; j < UY; ++j) {
-        if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
-        const float dy = (fy + (float)(UH * j)) - r.my;
-        const bool row_in = ry0 + UH * j + ly < H;
+        for (int j = 0; j < UY; ++j) {
+          if (!(um & (((1u << UX) - 1u) << (j * UX)))) continue;
+          const float dy = (fy + (float)(UH * j)) - r.my;
+          const bool row_in = ry0 + UH * j + ly < H;
 #pragma unroll
-        for (int i = 0; i < UX; ++i) {
-          if (!(um & (1u << (j * UX + i)))) continue;
-          const float dx = (fx + (float)(UW * i)) - r.mx;
-          const float u1 = r.l11 * dx + r.l12 * dy;
-          const float u2 = r.l21 * dx + r.l22 * dy;
-          const float q = u1 * u1 + u2 * u2;
-          const bool in_frame = row_in && tx0 + UW * i + lx < W;
-          n_in += __popcll(__builtin_amdgcn_ballot_w64(q <= thr && in_frame));
+          for (int i = 0; i < UX; ++i) {
+            if (!(um & (1u << (j * UX + i)))) continue;
+            const float dx = (fx + (float)(UW * i)) - r.mx;
+            float u1, u2;
+            whiten<THIN>(r.l11, r.l12, r.l21, r.l22, tx, dx, dy, u1, u2);
+            const float q = u1 * u1 + u2 * u2;
+            const bool in_frame = row_in && tx0 + UW * i + lx < W;
+            n_in += __popcll(__builtin_amdgcn_ballot_w64(q <= thr && in_frame));
+          }
         }
       }
-    }
+    };
+    run(IC<0>{}, 0, np);
+    run(IC<1>{}, np, __builtin_amdgcn_readfirstlane(cnt));
   }
   if (lane == 0 && n_in) atomicAdd(count, n_in);
 }
@@ -342,9 +438,12 @@ __global__ void k_zero_count(unsigned long long *count) { *count = 0ull; }
 // Fewer VALU instructions than the transposed butterfly, but two LDS round
 // trips per list entry: measured 8% faster for one channel (K = 6) and
 // 4-6% slower from three channels up, so it serves CP == 1 only.
+#ifndef PDR_XPOSE_ONE_CHANNEL
+#define PDR_XPOSE_ONE_CHANNEL 1
+#endif
 template <int CP>
 struct UseXpose {
-  static constexpr bool value = CP == 1;
+  static constexpr bool value = CP == 1 && PDR_XPOSE_ONE_CHANNEL;
 };
 constexpr int kRedRow = kWave + 4;
 template <int K, int KP>
@@ -366,9 +465,6 @@ __device__ __forceinline__ float wave_reduce_xpose(const float *v, float *red, i
   if constexpr (GL >= 8) r += dpp_row_shl<4>(r);  // lane 8 g reads lane 8 g + 4
   return r;
 }
-
-template <int V>
-using IC = std::integral_constant<int, V>;
 
 // Calls fn(IC<u>, IC<1>) for the lowest unit u of the mask um (non-empty),
 // then fn(IC<v>, IC<0>) for every later unit v in um, each with its index
@@ -401,10 +497,11 @@ struct Pow2Up {
 
 template <int CP, int UW, int UX, int UY>
 __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward(
-    const GRec *__restrict__ recs, const float *__restrict__ params,
-    const void *__restrict__ gimg, const int *__restrict__ tile_off,
+    const GRec *__restrict__ recs, const ThinRec *__restrict__ thin,
+    const float *__restrict__ params, const void *__restrict__ gimg,
+    const int *__restrict__ tile_off,
     const int *__restrict__ list, int B, int N, int H, int W, int C, int c0, int cc, float thr,
-    int nTx, int nT, float *__restrict__ sums, ImgView iv, const WsHeader *hdr,
+    int nTx, int nT, float *__restrict__ sums, ImgView iv, WsHeader *hdr,
     const int *__restrict__ order) {
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
@@ -416,6 +513,8 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
             : !xcd_frame_item(blockIdx.x, nT, B, &f, &t))
     return;
   __shared__ Entry<CP> s[WL::kBatch];
+  __shared__ ThinX sx[WL::kBatch];
+  __shared__ int scnt[2 * WL::kWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int tx0 = (t % nTx) * kTileW, ty0 = (t / nTx) * kTileH;
@@ -445,6 +544,25 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
       }
     }
   }
+  // Non-finite dL/dI.  The evaluation multiplies every lane's G by its
+  // weight, and a lane outside the truncation (w = 0) would turn a NaN or an
+  // infinity there into NaN.  So the raster takes non-finite values as 0 and
+  // flags their presence in the workspace header; the finalisation then adds
+  // the terms of those values on the pixels of each Gaussian's support, so
+  // that a non-finite value reaches exactly the sums of the Gaussians whose
+  // support holds its pixel.
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < UY; ++j)
+#pragma unroll
+    for (int i = 0; i < UX; ++i)
+#pragma unroll
+      for (int c = 0; c < CP; ++c) {
+        const bool fin = __builtin_isfinite(G[j][i][c]);
+        bad |= !fin;
+        G[j][i][c] = fin ? G[j][i][c] : 0.f;
+      }
+  if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) hdr->nonfinite = 1;
   // which value's wave total a lane holds after the reduction, and whether
   // it issues that value's atomic
   constexpr bool kXpose = UseXpose<CP>::value;
@@ -470,77 +588,90 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
-    stage_entry<CP, UW>(s, recs, params, list, s0, cnt, gbase, P, c0, cc, tid, tx0, ty0, thr);
+    const int np = stage_batch<CP, UW, WL::kWaves, false>(s, sx, scnt, recs, thin, params, list, s0, cnt,
+                                                   gbase, P, c0, cc, tid, tx0, ty0, thr);
     __syncthreads();
-    // the entry loop runs on a scalar count; each entry is read whole (its
-    // unit mask is all but never empty for a listed Gaussian)
-    const int ecnt = __builtin_amdgcn_readfirstlane(cnt);
-    for (int e = 0; e < ecnt; ++e) {
-      const Entry<CP> r = s[e];
-      const unsigned int um =
-          (__builtin_amdgcn_readfirstlane(r.mask) >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
-      if (um == 0u) continue;
-      float a[CP];
+    // the entry loops run on scalar counts; each entry is read whole (its
+    // unit mask is all but never empty for a listed Gaussian).  THIN: the
+    // compensated evaluation of the batch's thin entries, after the others.
+    auto run = [&](auto thinc, int e0, int e1) {
+      constexpr bool THIN = decltype(thinc)::value != 0;
+      for (int e = e0; e < e1; ++e) {
+        const Entry<CP> r = s[e];
+        const unsigned int fl = __builtin_amdgcn_readfirstlane(r.mask);
+        const unsigned int um = (fl >> mshift) & ((1u << WL::kUnitsPerWave) - 1u);
+        if (um == 0u) continue;
+        ThinX tx{};
+        if constexpr (THIN) tx = uniform(sx[e]);
+        float a[CP];
 #pragma unroll
-      for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
-      // The first unit of the mask assigns the partial sums (no zeroing);
-      // the later ones add to them and are skipped when no lane of the unit
-      // lies inside the truncation.
-      float part[KP];
+        for (int c = 0; c < CP; ++c) a[c] = r.amp[c];
+        // The first unit of the mask assigns the partial sums (no zeroing);
+        // the later ones add to them and are skipped when no lane of the
+        // unit lies inside the truncation.
+        float part[KP];
 #pragma unroll
-      for (int k = K; k < KP; ++k) part[k] = 0.f;
-      bool any = false;
-      auto unit = [&](auto uc, auto firstc) {
-        constexpr int u = decltype(uc)::value, j = u / UX, i = u % UX;
-        constexpr bool first = decltype(firstc)::value != 0;
-        const float dy = (fy + (float)(UH * j)) - r.my;
-        const float dx = (fx + (float)(UW * i)) - r.mx;
-        const float u1 = r.l11 * dx + r.l12 * dy;
-        const float u2 = r.l21 * dx + r.l22 * dy;
-        const float q = u1 * u1 + u2 * u2;
-        const bool inside = q <= thr;
-        const bool hit = __builtin_amdgcn_ballot_w64(inside) != 0ull;
-        if (!first && !hit) return;
-        any |= hit;
-        const float w = inside ? __builtin_amdgcn_exp2f(-q) : 0.f;
-        float h = G[j][i][0] * a[0];
+        for (int k = K; k < KP; ++k) part[k] = 0.f;
+        bool any = false;
+        auto unit = [&](auto uc, auto firstc) {
+          constexpr int u = decltype(uc)::value, j = u / UX, i = u % UX;
+          constexpr bool first = decltype(firstc)::value != 0;
+          const float dy = (fy + (float)(UH * j)) - r.my;
+          const float dx = (fx + (float)(UW * i)) - r.mx;
+          float u1, u2;
+          whiten<THIN>(r.l11, r.l12, r.l21, r.l22, tx, dx, dy, u1, u2);
+          const float q = u1 * u1 + u2 * u2;
+          const bool inside = q <= thr;
+          const bool hit = __builtin_amdgcn_ballot_w64(inside) != 0ull;
+          if (!first && !hit) return;
+          any |= hit;
+          const float w = inside ? __builtin_amdgcn_exp2f(-q) : 0.f;
+          float h = G[j][i][0] * a[0];
 #pragma unroll
-        for (int c = 1; c < CP; ++c) h += G[j][i][c] * a[c];
-        const float v = h * w;
-        const float t1 = v * u1, t2 = v * u2;
-        if constexpr (first) {
+          for (int c = 1; c < CP; ++c) h += G[j][i][c] * a[c];
+          const float v = h * w;
+          const float t1 = v * u1, t2 = v * u2;
+          if constexpr (first) {
 #pragma unroll
-          for (int c = 0; c < CP; ++c) part[c] = G[j][i][c] * w;
-          part[CP + 0] = t1;
-          part[CP + 1] = t2;
-          part[CP + 2] = t1 * u1;
-          part[CP + 3] = t2 * u2;
-          part[CP + 4] = t1 * u2;
+            for (int c = 0; c < CP; ++c) part[c] = G[j][i][c] * w;
+            part[CP + 0] = t1;
+            part[CP + 1] = t2;
+            part[CP + 2] = t1 * u1;
+            part[CP + 3] = t2 * u2;
+            part[CP + 4] = t1 * u2;
+          } else {
+#pragma unroll
+            for (int c = 0; c < CP; ++c) part[c] += G[j][i][c] * w;
+            part[CP + 0] += t1;
+            part[CP + 1] += t2;
+            part[CP + 2] += t1 * u1;
+            part[CP + 3] += t2 * u2;
+            part[CP + 4] += t1 * u2;
+          }
+        };
+        for_units_from_first<WL::kUnitsPerWave>(um, unit);
+        if (!any) continue;
+        // a thin entry with swapped rows accumulated S2, S1, S22, S11, S12
+        const bool sw = THIN && (fl & kEntrySwap);
+        auto swapped = [&](int sl) { return (sw && sl >= 0 && sl < 4) ? sl ^ 1 : sl; };
+        if constexpr (kSplit) {
+          // part[16..20] are the moments, part[21..23] zero
+          const float tot = wave_reduce_transposed<16>(part, lane);
+          const float tot_m = wave_reduce_transposed<8>(part + 16, lane);
+          const int sm = swapped(slot_m);
+          if (slot >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot), tot);
+          if (sm >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + sm), tot_m);
         } else {
-#pragma unroll
-          for (int c = 0; c < CP; ++c) part[c] += G[j][i][c] * w;
-          part[CP + 0] += t1;
-          part[CP + 1] += t2;
-          part[CP + 2] += t1 * u1;
-          part[CP + 3] += t2 * u2;
-          part[CP + 4] += t1 * u2;
+          float tot;
+          if constexpr (kXpose) tot = wave_reduce_xpose<K, KP>(part, red, lane);
+          else tot = wave_reduce_transposed<KP>(part, lane);
+          const int sl = swapped(slot);
+          if (sl >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + sl), tot);
         }
-      };
-      for_units_from_first<WL::kUnitsPerWave>(um, unit);
-      if (!any) continue;
-      if constexpr (kSplit) {
-        // part[16..20] are the moments, part[21..23] zero
-        const float tot = wave_reduce_transposed<16>(part, lane);
-        const float tot_m = wave_reduce_transposed<8>(part + 16, lane);
-        if (slot >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot), tot);
-        if (slot_m >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot_m), tot_m);
-      } else {
-        float tot;
-        if constexpr (kXpose) tot = wave_reduce_xpose<K, KP>(part, red, lane);
-        else tot = wave_reduce_transposed<KP>(part, lane);
-        if (slot >= 0) unsafeAtomicAdd(sums + (unsigned)(r.row + slot), tot);
       }
-    }
+    };
+    run(IC<0>{}, 0, np);
+    run(IC<1>{}, np, __builtin_amdgcn_readfirstlane(cnt));
   }
 }
 
@@ -551,22 +682,61 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
 // undoing the kappa scale of the whitened coordinates.  A Gaussian with an
 // empty pixel box (culled, or with no pixel in the frame) is in no tile
 // list: its row was zeroed and stays zero, so only its 8-byte box is read.
+// When the raster met a non-finite dL/dI value (which it took as 0), the
+// terms of such values on the Gaussian's support are added first: for
+// every pixel of its box holding one inside the truncation (the
+// definition's q, fp64), G_c w for the non-finite channels and, with
+// X = sum of G_c a_c over them, X w times each moment.  The sums then carry
+// the IEEE result of the full sum (finite + inf = inf, inf - inf = NaN).
 __global__ __launch_bounds__(256) void k_finalize(const float *__restrict__ params,
                                                   const uint2 *__restrict__ boxes,
-                                                  float *__restrict__ grad, long long BN, int C,
-                                                  const WsHeader *hdr) {
+                                                  float *__restrict__ grad, long long BN, int N,
+                                                  int C, const WsHeader *hdr,
+                                                  const void *__restrict__ gimg, int ldo, int ooff,
+                                                  int fmt, int H, int W, double k2) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= BN) return;
   if (hdr->status & (kStatusOverflow | kStatusStale)) return;
   const uint2 bx = boxes[i];
-  if ((bx.x & 0xFFFFu) > (bx.x >> 16) || (bx.y & 0xFFFFu) > (bx.y >> 16)) return;
+  const int x0 = (int)(bx.x & 0xFFFFu), x1 = (int)(bx.x >> 16);
+  const int y0 = (int)(bx.y & 0xFFFFu), y1 = (int)(bx.y >> 16);
+  if (x0 > x1 || y0 > y1) return;
   const int P = 5 + C;
   const float *g = params + i * P;
   float *o = grad + i * P;
   double sn, cs;
   sincos((double)g[4], &sn, &cs);
   const double s1 = g[2], s2 = g[3];
-  const double S1 = o[0], S2 = o[1], S11 = o[2], S22 = o[3], S12 = o[4];
+  double S1 = o[0], S2 = o[1], S11 = o[2], S22 = o[3], S12 = o[4];
+  if (hdr->nonfinite) {
+    const long long f = i / N;
+    for (int y = y0; y <= y1; ++y) {
+      for (int x = x0; x <= x1; ++x) {
+        const size_t base = (((size_t)f * H + y) * W + x) * (size_t)ldo + ooff;
+        bool any = false;
+        for (int c = 0; c < C; ++c) any |= !__builtin_isfinite(load_image(gimg, base + c, fmt));
+        if (!any) continue;
+        const double dx = (x + 0.5) - (double)g[0], dy = (y + 0.5) - (double)g[1];
+        const double z1 = (cs * dx + sn * dy) / s1, z2 = (-sn * dx + cs * dy) / s2;
+        const double q = z1 * z1 + z2 * z2;
+        if (!(q <= k2)) continue;
+        const double w = exp(-0.5 * q);
+        double X = 0.0;
+        for (int c = 0; c < C; ++c) {
+          const double gv = load_image(gimg, base + c, fmt);
+          if (__builtin_isfinite(gv)) continue;
+          o[5 + c] = (float)((double)o[5 + c] + gv * w);
+          X += gv * (double)g[5 + c];
+        }
+        const double v = X * w, a1 = kKappa * z1, a2 = kKappa * z2;
+        S1 += v * a1;
+        S2 += v * a2;
+        S11 += v * a1 * a1;
+        S22 += v * a2 * a2;
+        S12 += v * a1 * a2;
+      }
+    }
+  }
   o[0] = (float)(((cs / s1) * S1 - (sn / s2) * S2) / kKappa);
   o[1] = (float)(((sn / s1) * S1 + (cs / s2) * S2) / kKappa);
   o[2] = (float)(S11 / (kKappa2 * s1));
@@ -581,6 +751,7 @@ __global__ __launch_bounds__(256) void k_zero_verify(float *__restrict__ p, long
                                                      int W, int C, float radius,
                                                      unsigned long long ptr) {
   if (blockIdx.x == 0 && threadIdx.x == 0) {
+    hdr->nonfinite = 0;
     int st = hdr->status & ~kStatusStale;
     if (check) {
       bool same = hdr->stamp[0] == B && hdr->stamp[1] == N && hdr->stamp[2] == H &&
@@ -604,6 +775,7 @@ namespace {
 
 struct RasterArgs {
   const GRec *recs;
+  const ThinRec *thin;
   const float *params;
   const void *gimg;
   const int *tile_off;
@@ -623,8 +795,8 @@ void fwd_cp(const RasterArgs &a, hipStream_t st) {
   dim3 grid((unsigned)xcd_grid(a.nT, a.B));
   PDR_TIMED(PDR_K_FORWARD_RASTER, st,
             hipLaunchKernelGGL((k_forward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
-                               a.recs, a.params, a.tile_off, a.list, a.B, a.N, a.H, a.W, a.C,
-                               a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr, a.order));
+                               a.recs, a.thin, a.params, a.tile_off, a.list, a.B, a.N, a.H, a.W,
+                               a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr, a.order));
 }
 
 template <int CP, int UW, int UX, int UY>
@@ -633,9 +805,10 @@ void bwd_cp(const RasterArgs &a, hipStream_t st) {
   dim3 grid((unsigned)xcd_grid(a.nT, a.B));
   PDR_TIMED(PDR_K_BACKWARD_RASTER, st,
             hipLaunchKernelGGL((k_backward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
-                               a.recs, a.params, a.gimg, a.tile_off, a.list, a.B, a.N, a.H, a.W,
-                               a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, static_cast<float *>(a.out),
-                               a.iv, a.hdr, a.order));
+                               a.recs, a.thin, a.params, a.gimg, a.tile_off, a.list, a.B, a.N,
+                               a.H, a.W, a.C, a.c0, a.cc, a.thr, a.nTx, a.nT,
+                               static_cast<float *>(a.out),
+                               a.iv, const_cast<WsHeader *>(a.hdr), a.order));
 }
 
 // Unit shape and units per wave (compile-time tuning knob): 8x8 quads,
@@ -675,6 +848,7 @@ RasterArgs raster_args(const float *params, int B, int N, int H, int W, int C, f
   char *w = (char *)ws;
   RasterArgs a;
   a.recs = (const GRec *)(w + L.recs);
+  a.thin = (const ThinRec *)(w + L.thin);
   a.params = params;
   a.gimg = nullptr;
   a.tile_off = (const int *)(w + L.tile_off);
@@ -716,8 +890,8 @@ hipError_t launch_count_support(const float *params, int B, int N, int H, int W,
   using WL = WaveLayout<UW, UX, UY>;
   hipLaunchKernelGGL(k_zero_count, dim3(1), dim3(1), 0, st, count);
   hipLaunchKernelGGL((k_count_support<UW, UX, UY>), dim3((unsigned)xcd_grid(a.nT, a.B)),
-                     dim3(WL::kThreads), 0, st, a.recs, a.params, a.tile_off, a.list, a.B, a.N,
-                     a.H, a.W, a.C, a.thr, a.nTx, a.nT, count, a.hdr);
+                     dim3(WL::kThreads), 0, st, a.recs, a.thin, a.params, a.tile_off, a.list, a.B,
+                     a.N, a.H, a.W, a.C, a.thr, a.nTx, a.nT, count, a.hdr);
   return hipGetLastError();
 }
 
@@ -744,8 +918,9 @@ hipError_t launch_backward(const float *params, const void *grad_image, float *g
   }
   PDR_TIMED(PDR_K_FINALIZE, st,
             hipLaunchKernelGGL(k_finalize, dim3((unsigned)((BN + 255) / 256)), dim3(256), 0, st,
-                               params, (const uint2 *)((char *)ws + L.boxes), grad_params, BN,
-                               C, (const WsHeader *)hdr));
+                               params, (const uint2 *)((char *)ws + L.boxes), grad_params, BN, N,
+                               C, (const WsHeader *)hdr, grad_image, Cp + C, Cp, fmt, H, W,
+                               (double)radius * (double)radius));
   return hipGetLastError();
 }
 

@@ -74,7 +74,8 @@ struct SpanPow2 {
 
 template <int CP, int FMT>
 __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
-    const GRec *__restrict__ recs, const float *__restrict__ params, const void *__restrict__ gimg,
+    const GRec *__restrict__ recs, const ThinRec *__restrict__ thin,
+    const float *__restrict__ params, const void *__restrict__ gimg,
     int B, int N, int H, int W, int C, float thr, int items, float *__restrict__ grad,
     const WsHeader *hdr) {
   constexpr int K = CP + 5;
@@ -117,23 +118,47 @@ __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
     float part[KP];
 #pragma unroll
     for (int k = 0; k < KP; ++k) part[k] = 0.f;
-    // span quadratic in dx: qa dx^2 + 2 qb dy dx + qc dy^2 <= thr
+    // The row's span in closed form: with d = p - mu,
+    //   q(dx) = qa (dx - xc)^2 + qd dy^2,  xc = -(qb / qa) dy,  qd = det^2 / qa
+    // (qa = l11^2 + l21^2, qb = l11 l12 + l21 l22, det = l11 l22 - l12 l21, a
+    // sum of two terms of one sign), which loses nothing to cancellation
+    // where the expanded quadratic's discriminant loses u |L|^2 |d|^2 for
+    // thin Gaussians.  The span is widened by the rounding of its centre.
     const float qa = r.l11 * r.l11 + r.l21 * r.l21;
     const float qb = r.l11 * r.l12 + r.l21 * r.l22;
     const float qc = r.l12 * r.l12 + r.l22 * r.l22;
+    const float det = r.l11 * r.l22 - r.l12 * r.l21;
     const float inv_qa = 1.0f / qa;
+    const float xb = qb * inv_qa, qd = det * det * inv_qa;
+    const float xb_err = 2.4e-7f * sqrtf(qc * inv_qa);   // 4u sqrt(qc / qa) bounds |xb| rounding / |dy|
+    // a thin Gaussian takes the compensated evaluation about its split mean
+    // (rows in thin-row-last order; the sums of swapped rows trade places)
+    const bool thin_g = is_thin(r.l11, r.l12, r.l21, r.l22) && (thin[gi].flags & kThinOk);
+    ThinX tx{};
+    float l11 = r.l11, l12 = r.l12, l21 = r.l21, l22 = r.l22, mx = r.mx, my = r.my;
+    bool sw = false;
+    if (thin_g) {
+      const ThinRec tr = thin[gi];
+      sw = (tr.flags & kThinSwap) != 0;
+      if (sw) {
+        l11 = r.l21; l12 = r.l22; l21 = r.l11; l22 = r.l12;
+      }
+      mx = tr.mhx;
+      my = tr.mhy;
+      tx = ThinX{tr.lo21, tr.lo22, tr.c1, tr.c2};
+    }
 
     for (int ry = y0; ry <= y1; ry += kWave) {
       const int y = ry + lane;
       int len = 0, xs = 0;
       if (y <= y1) {
         const float dy = ((float)y + 0.5f) - r.my;
-        const float b = qb * dy;
-        const float disc = b * b - qa * (qc * dy * dy - thr_span);
-        if (disc >= 0.f) {
-          const float sq = sqrtf(disc);
-          const float lo = r.mx + (-b - sq) * inv_qa - 0.5f;
-          const float hi = r.mx + (-b + sq) * inv_qa - 0.5f;
+        const float rem = thr_span - qd * dy * dy;
+        if (rem >= 0.f) {
+          const float half = sqrtf(rem * inv_qa);
+          const float xc = r.mx - xb * dy - 0.5f;
+          const float pad = 1e-3f + xb_err * fabsf(dy) + 2.4e-7f * (fabsf(xc) + half);
+          const float lo = xc - half - pad, hi = xc + half + pad;
           xs = max(x0, (int)ceilf(lo));
           const int xe = min(x1, (int)floorf(hi));
           len = max(0, xe - xs + 1);
@@ -193,10 +218,11 @@ __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
           load_window(off_n, G_n);
         }
         if (off_c != kOff) {
-          const float dx = ((float)x_c + 0.5f) - r.mx;
-          const float dy = ((float)(ry + row_c) + 0.5f) - r.my;
-          const float u1 = r.l11 * dx + r.l12 * dy;
-          const float u2 = r.l21 * dx + r.l22 * dy;
+          const float dx = ((float)x_c + 0.5f) - mx;   // exact about a split mean
+          const float dy = ((float)(ry + row_c) + 0.5f) - my;
+          float u1, u2;
+          if (thin_g) whiten<true>(l11, l12, l21, l22, tx, dx, dy, u1, u2);
+          else whiten<false>(l11, l12, l21, l22, tx, dx, dy, u1, u2);
           const float q = u1 * u1 + u2 * u2;
           if (q <= thr) {
             const float w = __builtin_amdgcn_exp2f(-q);
@@ -222,7 +248,9 @@ __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
       }
     }
     const float tot = wave_reduce_transposed<KP>(part, lane);
-    if (reduce_issuer<KP>(lane)) st_sum[vidx] = tot;
+    // swapped rows accumulated (S2, S1, S22, S11, S12): back to row order
+    const int vs = (sw && vidx >= CP && vidx < CP + 4) ? CP + ((vidx - CP) ^ 1) : vidx;
+    if (reduce_issuer<KP>(lane)) st_sum[vs] = tot;
     // the chain rule (fp64), undoing the kappa scale of the whitened rows:
     //   dmu = L^T (S1, S2), ds1 = S11 / s1, ds2 = S22 / s2,
     //   dtheta = (s1/s2 - s2/s1) S12, da = A
@@ -268,25 +296,26 @@ __global__ void k_span_stamp(WsHeader *hdr, int check, int B, int N, int H, int 
 }
 
 template <int CP, int FMT>
-void launch_span_fmt(const GRec *recs, const float *params, const void *gimg, int B, int N, int H,
-                     int W, int C, float thr, float *grad, const WsHeader *hdr, hipStream_t st) {
+void launch_span_fmt(const GRec *recs, const ThinRec *thin, const float *params, const void *gimg,
+                     int B, int N, int H, int W, int C, float thr, float *grad, const WsHeader *hdr,
+                     hipStream_t st) {
   const int items = (N + kSpanPerBlock - 1) / kSpanPerBlock;
   PDR_TIMED(PDR_K_BACKWARD_RASTER, st,
             hipLaunchKernelGGL((k_backward_span<CP, FMT>), dim3((unsigned)xcd_grid(items, B)),
-                               dim3(kSpanThreads), 0, st, recs, params, gimg, B, N, H, W, C, thr,
-                               items, grad, hdr));
+                               dim3(kSpanThreads), 0, st, recs, thin, params, gimg, B, N, H, W, C,
+                               thr, items, grad, hdr));
 }
 
 template <int CP>
-void launch_span_cp(const GRec *recs, const float *params, const void *gimg, int fmt, int B, int N,
-                    int H, int W, int C, float thr, float *grad, const WsHeader *hdr,
-                    hipStream_t st) {
+void launch_span_cp(const GRec *recs, const ThinRec *thin, const float *params, const void *gimg,
+                    int fmt, int B, int N, int H, int W, int C, float thr, float *grad,
+                    const WsHeader *hdr, hipStream_t st) {
   if (fmt == PDR_FMT_F16)
-    launch_span_fmt<CP, PDR_FMT_F16>(recs, params, gimg, B, N, H, W, C, thr, grad, hdr, st);
+    launch_span_fmt<CP, PDR_FMT_F16>(recs, thin, params, gimg, B, N, H, W, C, thr, grad, hdr, st);
   else if (fmt == PDR_FMT_BF16)
-    launch_span_fmt<CP, PDR_FMT_BF16>(recs, params, gimg, B, N, H, W, C, thr, grad, hdr, st);
+    launch_span_fmt<CP, PDR_FMT_BF16>(recs, thin, params, gimg, B, N, H, W, C, thr, grad, hdr, st);
   else
-    launch_span_fmt<CP, PDR_FMT_F32>(recs, params, gimg, B, N, H, W, C, thr, grad, hdr, st);
+    launch_span_fmt<CP, PDR_FMT_F32>(recs, thin, params, gimg, B, N, H, W, C, thr, grad, hdr, st);
 }
 
 }  // namespace
@@ -301,17 +330,18 @@ hipError_t launch_backward_span(const float *params, const void *grad_image, flo
   char *w = (char *)ws;
   WsHeader *hdr = (WsHeader *)(w + L.hdr);
   const GRec *recs = (const GRec *)(w + L.recs);
+  const ThinRec *thin = (const ThinRec *)(w + L.thin);
   // stamp check only (nothing to zero: every gradient row is stored once)
   PDR_TIMED(PDR_K_ZERO, st,
             hipLaunchKernelGGL(k_span_stamp, dim3(1), dim3(64), 0, st, hdr, check_stamp ? 1 : 0, B,
                                N, H, W, C, radius, (unsigned long long)(uintptr_t)params));
   const float thr = (float)((double)radius * (double)radius * kKappa2);
-  if (C <= 1) launch_span_cp<1>(recs, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
-  else if (C == 2) launch_span_cp<2>(recs, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
-  else if (C == 3) launch_span_cp<3>(recs, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
-  else if (C == 4) launch_span_cp<4>(recs, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
-  else if (C <= 8) launch_span_cp<8>(recs, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
-  else launch_span_cp<16>(recs, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
+  if (C <= 1) launch_span_cp<1>(recs, thin, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
+  else if (C == 2) launch_span_cp<2>(recs, thin, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
+  else if (C == 3) launch_span_cp<3>(recs, thin, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
+  else if (C == 4) launch_span_cp<4>(recs, thin, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
+  else if (C <= 8) launch_span_cp<8>(recs, thin, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
+  else launch_span_cp<16>(recs, thin, params, grad_image, fmt, B, N, H, W, C, thr, grad_params, hdr, st);
   return hipGetLastError();
 }
 

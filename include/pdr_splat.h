@@ -22,7 +22,10 @@
  * truncation in units of sigma.  A Gaussian is invalid -- contributes nothing
  * and gets a zero gradient -- if any of its 5 + C values is not finite or if
  * s1 <= 0 or s2 <= 0.  The backward returns dL/dparams for a given dL/dimage
- * (the truncation indicator is not differentiated).
+ * (the truncation indicator is not differentiated).  Arithmetic is fp32;
+ * Gaussians of anisotropy above 8:1 have their thin whitened coordinate
+ * evaluated with compensation (a float pair), which keeps its error relative
+ * to its own size however thin the Gaussian.
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers (hipMalloc / torch), fp32 or
@@ -72,9 +75,10 @@ int pdr_splat_bin_variant(int B, int N, int H, int W);
 
 /* Bytes of workspace for a problem and a (tile, Gaussian) pair capacity.
  * Returns a negative pdr_status on invalid sizes.  The fixed part covers a
- * 256-byte header, 40 bytes per Gaussian, 16 bytes per tile and 256 KiB for
- * ordering the tiles by list length (each region rounded up to 256 bytes);
- * every pair takes 4 more bytes.  max_pairs <= 2^31 - 1.
+ * 256-byte header, 72 bytes per Gaussian (its raster record, the
+ * compensation constants of a thin one, its pixel box), 16 bytes per tile
+ * and 256 KiB for ordering the tiles by list length (each region rounded up
+ * to 256 bytes); every pair takes 4 more bytes.  max_pairs <= 2^31 - 1.
  * Problems with many Gaussians per frame on frames of many tile bands
  * (N >= 16384 where a frame's bands would each scan all of its boxes) bin
  * in two levels: first per tile row, then per tile from the row's list.
@@ -99,7 +103,10 @@ int pdr_splat_forward(const float *params, float *image, int B, int N, int H, in
  * reuse_binning = 1 uses the lists of the last forward on this workspace;
  * the workspace records (B, N, H, W, C, radius, params) at binning and a
  * mismatch is flagged as PDR_ERR_STALE.  The caller must not have changed
- * the parameter values in between.  reuse_binning = 0 bins again. */
+ * the parameter values in between.  reuse_binning = 0 bins again.
+ * A non-finite grad_image value (NaN, +-inf) enters exactly the gradients of
+ * the Gaussians whose truncated support holds its pixel, as it would in the
+ * IEEE sum of their terms; every other gradient is unaffected. */
 int pdr_splat_backward(const float *params, const float *grad_image, float *grad_params, int B,
                        int N, int H, int W, int C, float radius, void *workspace,
                        size_t workspace_bytes, int reuse_binning, void *stream);

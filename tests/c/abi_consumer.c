@@ -28,13 +28,14 @@ int main(void) {
     const int t = pdr_splat_tile_size();
     CHECK(t == 16 || t == 32);
 
-    /* fixed part: header, 32-byte records, 8-byte boxes, per-tile counts,
-     * per-tile group totals, tile offsets, the tile order, the 64 KiB order
-     * histogram; then 4 bytes per pair */
+    /* fixed part: header, 32-byte records, 32-byte thin-Gaussian records,
+     * 8-byte boxes, per-tile counts, per-tile group totals, tile offsets, the
+     * tile order, the 256 KiB order histogram; then 4 bytes per pair */
     {
         const int B = 2, N = 100, H = 40, W = 72, C = 3;
         const long long nTx = (W + t - 1) / t, nTy = (H + t - 1) / t, nT = B * nTx * nTy;
         const long long fixed = round256(256) + round256((long long)B * N * 32) +
+                                round256((long long)B * N * 32) +
                                 round256((long long)B * N * 8) + round256(nT * 4) +
                                 round256(nT * 4) + round256((nT + 1) * 4) + round256(nT * 4) +
                                 262144;

@@ -12,7 +12,7 @@ import pytest
 
 from differentiable_gaussian_splatting_pdr_amd import workloads
 from oracle import adapter as oa
-from helpers import check_close
+from helpers import check_grad, check_close
 
 pytestmark = pytest.mark.gpu
 
@@ -101,7 +101,7 @@ def test_concat_fusion(orc, case):
     img, slk, _, _ = orc.render(params, H, W, 3.0)
     check_close(o[..., Cp:], img, np.abs(img), slk, "rendered part")
     gr, gsl, gmag = orc.grad(params, np.ascontiguousarray(gout[..., Cp:]), H, W, 3.0)
-    check_close(pt.grad.cpu().numpy(), gr, gmag, gsl, "grad params")
+    check_grad(pt.grad.cpu().numpy(), gr, gmag, gsl, "grad params")
     assert np.array_equal(xt.grad.cpu().numpy(), gout[..., :Cp])
     # the plain entry point on the same inputs gives the same rendered bits
     plain, _ = splat.forward(pt.detach(), H, W)
@@ -126,7 +126,7 @@ def test_concat_benchmark_shape_sampled_frames(orc):
         img, slk, _, _ = orc.render(params[f:f + 1], H, W, 3.0)
         check_close(o[f:f + 1, ..., Cp:], img, np.abs(img), slk, "frame %d" % f)
         gr, gsl, gmag = orc.grad(params[f:f + 1], grad[f:f + 1], H, W, 3.0)
-        check_close(gp[f:f + 1], gr, gmag, gsl, "grad frame %d" % f)
+        check_grad(gp[f:f + 1], gr, gmag, gsl, "grad frame %d" % f)
 
 
 def test_adapter_render_loss_chain(orc):

@@ -1,6 +1,6 @@
 """The tile-free (span) backward against the fp64 oracle, on the GPU, over
 the same cases as the tile path: ragged shapes, radii, invalid / tiny /
-huge / off-screen Gaussians, the five workloads (full batch, sampled frames),
+huge / off-screen Gaussians, needles, the five workloads (full batch),
 reduced-precision dL/dI, reuse and no reuse of the forward's records, and
 the stale-workspace report.  Same tolerance (helpers)."""
 import numpy as np
@@ -8,7 +8,8 @@ import pytest
 
 from differentiable_gaussian_splatting_pdr_amd import workloads
 
-from helpers import check_against_oracle, check_close, gpu_forward_backward, quantize
+from helpers import (check_grad, check_against_oracle, check_close, gpu_forward_backward,
+                     make_needles, quantize)
 from test_gpu_parity import SMALL
 
 pytestmark = pytest.mark.gpu
@@ -69,10 +70,19 @@ def test_span_tiny_and_thin_gaussians(orc):
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4])
 def test_span_workload_full_size(orc, idx):
+    # gradients on every frame (16 frames spread over the 512 x 512 batch)
     wl, p, g = workloads.make_inputs(idx)
     res = gpu_forward_backward(p, g, wl.H, wl.W, algo=span())
-    frames = sorted({0, wl.B // 2, wl.B - 1})
-    print(wl.name, check_against_oracle(orc, p, g, wl.H, wl.W, frames=frames, gpu=res))
+    frames = slice(None) if wl.B * wl.H * wl.W <= 192 * 128 * 256 else np.arange(0, wl.B, wl.B // 16)
+    gr, gsl, gmag = orc.grad(p[frames], g[frames], wl.H, wl.W)
+    print(wl.name, check_grad(res["grad"][frames], gr, gmag, gsl, wl.name + " span grad"))
+
+
+@pytest.mark.parametrize("radius", [1.0, 3.0])
+def test_span_needles(orc, radius):
+    p, g, H, W = make_needles()
+    res = gpu_forward_backward(p, g, H, W, radius, algo=span())
+    check_against_oracle(orc, p, g, H, W, radius, gpu=res)
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
@@ -88,7 +98,7 @@ def test_span_reduced_precision_grad(orc, fmt):
     gp = splat.backward(pt, torch.from_numpy(gq).to(dev).to(dt), wl.H, wl.W, workspace=ws,
                         reuse_binning=True, algo=span()).cpu().numpy()
     gr, gsl, gmag = orc.grad(p, gq, wl.H, wl.W, 3.0)
-    check_close(gp, gr, gmag, gsl, "span grad " + fmt)
+    check_grad(gp, gr, gmag, gsl, "span grad " + fmt)
 
 
 def test_span_matches_tile_backward():
@@ -150,7 +160,7 @@ def test_span_rebin_leaves_no_reusable_binning(orc):
                                  wl.W, wl.C, 3.0, ws.ptr, ws.nbytes, 1, _lib.PDR_BWD_TILE, st)
     assert _lib.pdr_splat_check(ws.ptr, st)[0] == _lib.PDR_OK
     gr, gsl, gmag = orc.grad(p, g, wl.H, wl.W)
-    check_close(gp.cpu().numpy(), gr, gmag, gsl, "grad after a fresh forward")
+    check_grad(gp.cpu().numpy(), gr, gmag, gsl, "grad after a fresh forward")
 
 
 def test_auto_choice(orc):
@@ -168,3 +178,18 @@ def test_auto_choice(orc):
     s = gpu_forward_backward(p, g, 32, 32, algo=span())["grad"]
     assert not np.array_equal(a, s) or np.array_equal(t, s)   # large: not the span walk
     check_against_oracle(orc, p, g, 32, 32, gpu=gpu_forward_backward(p, g, 32, 32, algo=None))
+
+
+def test_span_nonfinite_grad_image(orc):
+    from test_gpu_parity import check_nonfinite, nonfinite_grad_image
+    p, g, H, W = nonfinite_grad_image()
+    res = gpu_forward_backward(p, g, H, W, algo=span())
+    print("Gaussians reached by non-finite dL/dI:", check_nonfinite(orc, p, g, H, W, res))
+
+
+@pytest.mark.parametrize("R", [4, 10, 16, 100])
+def test_span_anisotropy_sweep(orc, R):
+    from test_gpu_parity import anisotropy_case
+    p, g, H, W = anisotropy_case(R, 100 * R)
+    res = gpu_forward_backward(p, g, H, W, algo=span())
+    check_against_oracle(orc, p, g, H, W, gpu=res)
