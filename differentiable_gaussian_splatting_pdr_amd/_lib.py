@@ -26,6 +26,8 @@ EXPORTED = (
     "pdr_splat_count_support",
     "pdr_splat_workspace_bytes",
     "pdr_splat_forward",
+    "pdr_splat_forward_noalloc",
+    "pdr_splat_noalloc_scratch_bytes",
     "pdr_splat_backward",
     "pdr_splat_bin",
     "pdr_splat_check",
@@ -86,6 +88,10 @@ def lib() -> ctypes.CDLL:
         L.pdr_splat_workspace_bytes.restype = ll
         L.pdr_splat_forward.argtypes = [vp, vp, i, i, i, i, i, f, vp, sz, vp]
         L.pdr_splat_forward.restype = i
+        L.pdr_splat_forward_noalloc.argtypes = [vp, vp, i, i, i, i, i, f, vp, vp]
+        L.pdr_splat_forward_noalloc.restype = i
+        L.pdr_splat_noalloc_scratch_bytes.argtypes = []
+        L.pdr_splat_noalloc_scratch_bytes.restype = ll
         L.pdr_splat_backward.argtypes = [vp, vp, vp, i, i, i, i, i, f, vp, sz, i, vp]
         L.pdr_splat_backward.restype = i
         L.pdr_splat_bin.argtypes = [vp, i, i, i, i, i, f, vp, vp, ll, vp, sz, vp]
@@ -162,6 +168,17 @@ def pdr_splat_workspace_bytes(B, N, H, W, C, max_pairs) -> int:
 def pdr_splat_forward(params, image, B, N, H, W, C, radius, workspace, workspace_bytes, stream):
     return _raise(lib().pdr_splat_forward(params, image, B, N, H, W, C, float(radius), workspace,
                                           workspace_bytes, stream), "pdr_splat_forward")
+
+
+def pdr_splat_forward_noalloc(params, image, B, N, H, W, C, radius, status, stream):
+    """Forward with the library's static per-GPU scratch (no workspace, no
+    allocation); status: device pointer to one int (PDR_OK / PDR_ERR_OVERFLOW)."""
+    return _raise(lib().pdr_splat_forward_noalloc(params, image, B, N, H, W, C, float(radius),
+                                                  status, stream), "pdr_splat_forward_noalloc")
+
+
+def pdr_splat_noalloc_scratch_bytes() -> int:
+    return int(lib().pdr_splat_noalloc_scratch_bytes())
 
 
 def pdr_splat_backward(params, grad_image, grad_params, B, N, H, W, C, radius, workspace,

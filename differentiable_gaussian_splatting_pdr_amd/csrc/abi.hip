@@ -4,11 +4,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pdr_common.hpp"
 #include "pdr_internal.hpp"
 #include "pdr_splat.h"
 
 using namespace pdr;
+
+// The allocation-free forward's scratch (see below): 64 MiB per device.
+constexpr size_t kScratchBytes = 64u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -143,6 +149,40 @@ int validate_grid(int B, int gx, int gy, int H, int W, int C) {
   return PDR_OK;
 }
 
+// ----------------------------------------------------------------------------
+// The allocation-free forward: the library's own scratch, one per device.
+//
+// `scratch` (top of this file) is a file-scope device array.  In host code
+// its name is a
+// host-side stand-in, not a device address: the device address is obtained
+// once per device with hipGetSymbolAddress (the device current at the
+// time) and kept in scratch_ptr[device]; only that pointer is ever passed to
+// a kernel.
+
+constexpr int kScratchDevices = 64;
+
+std::mutex scratch_mu;
+void *scratch_ptr[kScratchDevices];
+
+// The scratch's device address on the current device (nullptr on failure).
+void *scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+// The overflow status of the last binning in a workspace header, as a
+// pdr_status in *out (device).
+__global__ void k_status_out(const WsHeader *hdr, int *out) {
+  if (threadIdx.x == 0) *out = (hdr->status & kStatusOverflow) ? PDR_ERR_OVERFLOW : PDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,6 +208,25 @@ int pdr_splat_forward(const float *params, float *image, int B, int N, int H, in
   return forward_impl(params, nullptr, 0, image, B, N, H, W, C, radius, workspace, workspace_bytes,
                       stream);
 }
+
+int pdr_splat_forward_noalloc(const float *params, float *image, int B, int N, int H, int W, int C,
+                              float radius, int *status, void *stream) {
+  Dims d;
+  if (!params || !image || !status) return PDR_ERR_INVALID_ARG;
+  int rc = validate_sizes(B, N, H, W, C, &d);
+  if (rc == PDR_OK) rc = validate_radius(radius);
+  if (rc != PDR_OK) return rc;
+  if (make_layout(d.BN, d.BT, 0, d.rp).total > kScratchBytes) return PDR_ERR_WORKSPACE;
+  void *ws = scratch_for_current_device();
+  if (!ws) return PDR_ERR_HIP;
+  rc = forward_impl(params, nullptr, 0, image, B, N, H, W, C, radius, ws, kScratchBytes, stream);
+  if (rc != PDR_OK) return rc;
+  hipLaunchKernelGGL(k_status_out, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const WsHeader *)ws, status);
+  return hip_status(hipGetLastError());
+}
+
+long long pdr_splat_noalloc_scratch_bytes(void) { return (long long)kScratchBytes; }
 
 int pdr_splat_backward(const float *params, const float *grad_image, float *grad_params, int B,
                        int N, int H, int W, int C, float radius, void *workspace,

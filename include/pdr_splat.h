@@ -140,6 +140,26 @@ int pdr_splat_count_support(const float *params, int B, int N, int H, int W, int
  * last binning. */
 int pdr_splat_check(void *workspace, void *stream, long long *pairs_needed);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the forward
+ * of pdr_splat_forward with the library's own scratch in place of a
+ * workspace.  The scratch is a static device array of
+ * pdr_splat_noalloc_scratch_bytes() = 64 MiB per GPU, held from the library's
+ * load until the process ends; the call allocates nothing.  It holds the
+ * fixed part of pdr_splat_workspace_bytes and as many pairs as fit: a
+ * problem whose fixed part exceeds it is rejected with PDR_ERR_WORKSPACE
+ * before anything runs (e.g. 384 frames x 4096 Gaussians do not fit; 160 x
+ * 1024 do), and one whose (tile, Gaussian) pairs exceed what remains leaves
+ * the image undefined and writes PDR_ERR_OVERFLOW to *status.  status: a
+ * DEVICE pointer to one int, overwritten with PDR_OK or PDR_ERR_OVERFLOW in
+ * stream order.  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (other streams, other threads) race; calls ordered on
+ * one stream do not.  The scratch keeps the last call's binning, but no
+ * backward can reuse it. */
+int pdr_splat_forward_noalloc(const float *params, float *image, int B, int N, int H, int W, int C,
+                              float radius, int *status, void *stream);
+long long pdr_splat_noalloc_scratch_bytes(void);
+
 /* Static description of a status code. */
 const char *pdr_splat_status_string(int status);
 
