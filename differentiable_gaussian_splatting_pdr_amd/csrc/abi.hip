@@ -112,11 +112,12 @@ int backward_impl(const float *params, const void *grad_image, int Cp, float *gr
   int rc = validate_sizes(B, N, H, W, C, &d);
   if (rc == PDR_OK) rc = validate_radius(radius);
   if (rc == PDR_OK && (long long)B * H * W * (Cp + (long long)C) > (1LL << 46)) rc = PDR_ERR_INVALID_ARG;
-  if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
   if (rc != PDR_OK) return rc;
   if (algo != PDR_BWD_AUTO && algo != PDR_BWD_TILE && algo != PDR_BWD_SPAN) return PDR_ERR_INVALID_ARG;
   const bool span_ok = Cp == 0 && span_backward_supported(H, W, C);
   if (algo == PDR_BWD_SPAN && !span_ok) return PDR_ERR_INVALID_ARG;
+  rc = layout_for(d, workspace, workspace_bytes, &L);   // arguments first, then the workspace
+  if (rc != PDR_OK) return rc;
   const bool span = algo == PDR_BWD_SPAN || (algo == PDR_BWD_AUTO && span_ok && auto_span(B, N));
   hipStream_t st = (hipStream_t)stream;
   char *w = (char *)workspace;

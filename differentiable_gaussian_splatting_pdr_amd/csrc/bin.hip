@@ -4,6 +4,8 @@
 //                 of the truncated ellipse q <= k^2, whitening rows (and the
 //                 compensation constants of thin Gaussians).
 //  k_bin<false,M,X> per (frame, tile group): per-tile overlap counts.
+//  k_count_scan     the groups' first list offsets (a linear scan of the
+//                   group totals) and the tile order's cursors.
 //  k_bin<true,M,X>  per (frame, tile group): the per-tile lists, ascending
 //                   Gaussian index, at the scanned offsets.
 //
@@ -140,6 +142,90 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
   return t;
 }
 
+// Between the count and write passes, one launch of 9 workgroups:
+//  * workgroups 0-7 (when the rasters take the tile order): XCD range r's
+//    order-key histogram becomes cursors -- its exclusive scan (keys
+//    ascending: longest first) plus the range's first slot, so that each
+//    entry is the next free position of its key in order[];
+//  * workgroup 8: the group totals gtot[0 .. ngroups) become their exclusive
+//    prefix, each write group's first list offset (clamped to int: any
+//    offset past that overflows the list capacity), in one linear pass; the
+//    pair total goes to the header with the overflow flag (a fresh binning
+//    clears any earlier overflow or stale flag).
+constexpr int kScanPer = 8;   // group totals per thread per round
+constexpr int kOrderPer = kOrderBuckets / kBinThreads;
+static_assert(kOrderBuckets % kBinThreads == 0, "whole keys per thread");
+__global__ __launch_bounds__(kBinThreads) void k_count_scan(int *__restrict__ gtot,
+                                                            long long ngroups, long long cap,
+                                                            WsHeader *hdr,
+                                                            int *__restrict__ ohist,
+                                                            unsigned int total_tiles) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x < 8) {
+    if (!ohist) return;
+    __shared__ int wtot[kBinThreads / kWave];
+    const int r = blockIdx.x;
+    const unsigned int per = (total_tiles + 7u) >> 3;
+    int *h = ohist + r * kOrderBuckets;
+    int v[kOrderPer], t = 0;
+#pragma unroll
+    for (int k = 0; k < kOrderPer; ++k) {
+      v[k] = h[tid * kOrderPer + k];
+      t += v[k];
+    }
+    const int incl = wave_incl_scan(t);
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    int wex = 0;
+    for (int w = 0; w < wave; ++w) wex += wtot[w];
+    int e = (int)((unsigned int)r * per) + wex + incl - t;
+#pragma unroll
+    for (int k = 0; k < kOrderPer; ++k) {
+      h[tid * kOrderPer + k] = e;
+      e += v[k];
+    }
+    return;
+  }
+  __shared__ long long wtl[kBinThreads / kWave];
+  long long carry = 0;
+  for (long long r0 = 0; r0 < ngroups; r0 += (long long)kBinThreads * kScanPer) {
+    const long long i0 = r0 + (long long)tid * kScanPer;
+    int v[kScanPer];
+    long long t = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      v[k] = i0 + k < ngroups ? gtot[i0 + k] : 0;
+      t += v[k];
+    }
+    long long incl = t;   // inclusive scan over the wave (64-bit)
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const long long o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) wtl[wave] = incl;
+    __syncthreads();
+    long long wex = 0, rtot = 0;
+    for (int w = 0; w < kBinThreads / kWave; ++w) {
+      wex += w < wave ? wtl[w] : 0;
+      rtot += wtl[w];
+    }
+    long long e = carry + wex + incl - t;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      if (i0 + k < ngroups) gtot[i0 + k] = (int)min(e, 0x7fffffffLL);
+      e += v[k];
+    }
+    carry += rtot;
+    __syncthreads();  // wtl is rewritten by the next round
+  }
+  if (tid == 0) {
+    hdr->total = carry;
+    hdr->cap = cap;
+    hdr->status = (carry > cap || carry > 0x7fffffffLL) ? kStatusOverflow : 0;
+  }
+}
+
 // LDS bit matrix binning.  Grid: G groups x B frames (1D, XCD-aware); a group
 // is a band of gh whole tile rows, or with ncc > 1 column chunks one tile row
 // of cw tiles (the last chunk narrower).  Either way its tiles are one
@@ -165,12 +251,12 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long *red) {
 // Count pass (WRITE = false): per-tile counts -- one LDS atomic add per
 // (box, group tile) overlap, over the boxes the group would scan -- and the
 // group's total.
-// Write pass (WRITE = true): the group's base offset is the sum of the
-// totals of all groups before it (frame-major, bands top to bottom); an
-// exclusive scan (wave64 DPP scan) of its tiles' counts gives their
-// offsets; then the lists are written through the chunks above.  The last
-// group writes the pair total and the overflow flag.  A tile's list length
-// is the number of boxes that meet it either way.
+// Write pass (WRITE = true): the group's base offset is the exclusive
+// prefix of the group totals (frame-major, bands top to bottom) that
+// k_count_scan left in gtot; an exclusive scan (wave64 DPP scan) of its
+// tiles' counts gives their offsets; then the lists are written through the
+// chunks above.  A tile's list length is the number of boxes that meet it
+// either way.
 constexpr int kSegSlots = 4;   // boxes per thread per member-scan segment
 
 template <bool WRITE, bool MEMBERS, bool COLS, bool ROWL = false>
@@ -232,11 +318,9 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
   }
 
   if (WRITE) {
-    // base of this group: totals of all groups before it
-    const long long gi = (long long)b * G + g;
-    long long part = 0;
-    for (long long k = tid; k < gi; k += kBinThreads) part += gtot[k];
-    const long long gbase = block_sum_ll(part, red);
+    // base of this group: the exclusive prefix of the group totals, which
+    // the count pass's last group left in gtot
+    const long long gbase = gtot[(size_t)b * G + g];
     // exclusive scan of the group's tile counts (2 * kBinThreads >= Tg)
     const int c0 = 2 * tid < Tg ? counts[t0 + 2 * tid] : 0;
     const int c1 = 2 * tid + 1 < Tg ? counts[t0 + 2 * tid + 1] : 0;
@@ -258,7 +342,7 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
       base[2 * tid + 1] = (int)min(e0 + c0, 0x7fffffffLL);
     }
     // longest-first raster order: each tile takes the next slot of its
-    // (XCD range, length bucket); the cursors come from k_order_scan
+    // (XCD range, length bucket); the cursors come from k_count_scan
     if (ohist) {
       const unsigned int total = (unsigned int)B * (unsigned int)nT;
       for (int k = 0; k < 2; ++k) {
@@ -269,13 +353,8 @@ __global__ __launch_bounds__(kBinThreads) void k_bin(const uint2 *__restrict__ b
     }
     const long long gend = gbase + gsum;
     const bool limit = gend > cap || gend > 0x7fffffffLL;
-    if (tid == 0 && b == B - 1 && g == G - 1) {
-      // a fresh binning: clears any earlier overflow or stale flag
-      tile_off[(size_t)B * nT] = (int)min(gend, 0x7fffffffLL);
-      hdr->total = gend;
-      hdr->cap = cap;
-      hdr->status = limit ? kStatusOverflow : 0;
-    }
+    if (tid == 0 && b == B - 1 && g == G - 1)
+      tile_off[(size_t)B * nT] = (int)min(hdr->total, 0x7fffffffLL);
     if (limit) return;  // uniform: this group's lists do not fit
   } else {
     for (int lt = tid; lt < Tg; lt += kBinThreads) base[lt] = 0;
@@ -631,35 +710,6 @@ __global__ __launch_bounds__(kBinThreads) void k_rowstart(int nTy, int *__restri
   if (tid == 0) fs[nTy] = (int)min(carry, 0x7fffffffLL);
 }
 
-// One workgroup per XCD range: exclusive scan of the range's key histogram
-// (keys ascending: longest first) in place, plus the range's first slot,
-// so that each entry becomes the next free position of its key in order[].
-constexpr int kOrderPer = kOrderBuckets / kBinThreads;
-static_assert(kOrderBuckets % kBinThreads == 0, "whole keys per thread");
-__global__ __launch_bounds__(kBinThreads) void k_order_scan(int *__restrict__ ohist,
-                                                            unsigned int total) {
-  __shared__ int wtot[kBinThreads / kWave];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int *h = ohist + r * kOrderBuckets;
-  int v[kOrderPer], t = 0;
-#pragma unroll
-  for (int k = 0; k < kOrderPer; ++k) {
-    v[k] = h[tid * kOrderPer + k];
-    t += v[k];
-  }
-  const int incl = wave_incl_scan(t);
-  if (lane == 63) wtot[wave] = incl;
-  __syncthreads();
-  int wex = 0;
-  for (int w = 0; w < wave; ++w) wex += wtot[w];
-  int e = (int)((unsigned int)r * ((total + 7u) >> 3)) + wex + incl - t;
-#pragma unroll
-  for (int k = 0; k < kOrderPer; ++k) {
-    h[tid * kOrderPer + k] = e;
-    e += v[k];
-  }
-}
-
 // ----------------------------------------------------------------------------
 // host launchers
 
@@ -866,9 +916,8 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
       hipLaunchKernelGGL(k_count, g2, dim3(kBinThreads), lds2, st, boxes, B, N, nTx, nTy, 1,
                          bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr, (int *)nullptr,
                          cap, hdr, ohist, order, (const int *)rlist, (const int *)fstart, L.cap);
-      if (ordered)
-        hipLaunchKernelGGL(k_order_scan, dim3(8), dim3(kBinThreads), 0, st, ohist,
-                           (unsigned)(B * nTx * nTy));
+      hipLaunchKernelGGL(k_count_scan, dim3(9), dim3(kBinThreads), 0, st, gtot,
+                         (long long)B * bg.G, cap, hdr, ohist, (unsigned)(B * nTx * nTy));
     });
     PDR_TIMED(PDR_K_BIN_WRITE, st,
               hipLaunchKernelGGL(k_write, g2, dim3(kBinThreads), lds2, st, boxes, B, N, nTx, nTy,
@@ -891,9 +940,8 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
     hipLaunchKernelGGL(k_count, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy, bg.gh,
                        bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr, (int *)nullptr,
                        cap, hdr, ohist, order, (const int *)nullptr, (const int *)nullptr, 0LL);
-    if (ordered)
-      hipLaunchKernelGGL(k_order_scan, dim3(8), dim3(kBinThreads), 0, st, ohist,
-                         (unsigned)(B * nTx * nTy));
+    hipLaunchKernelGGL(k_count_scan, dim3(9), dim3(kBinThreads), 0, st, gtot, (long long)B * bg.G,
+                       cap, hdr, ohist, (unsigned)(B * nTx * nTy));
   });
   PDR_TIMED(PDR_K_BIN_WRITE, st,
             hipLaunchKernelGGL(k_write, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,

@@ -176,7 +176,13 @@ constexpr unsigned int kEmptyBox = 0x0000FFFFu;  // x0 = 65535 > x1 = 0
 #ifndef PDR_ORDER_QUARTERS
 #define PDR_ORDER_QUARTERS 4
 #endif
-constexpr int kOrderClasses = 16, kOrderSub = 16, kOrderFine = 32;
+#ifndef PDR_ORDER_SUB
+#define PDR_ORDER_SUB 16
+#endif
+#ifndef PDR_ORDER_WINDOW_MAJOR
+#define PDR_ORDER_WINDOW_MAJOR 0
+#endif
+constexpr int kOrderClasses = 16, kOrderSub = PDR_ORDER_SUB, kOrderFine = 512 / PDR_ORDER_SUB;
 constexpr int kOrderQ = PDR_ORDER_QUARTERS;   // length steps of an octave taken before the windows
 constexpr int kOrderBuckets = kOrderClasses * kOrderSub * kOrderFine;   // keys per XCD range
 
@@ -192,6 +198,10 @@ __device__ __forceinline__ int order_key(int len, unsigned int pos, unsigned int
   const int sub = (int)(((unsigned long long)pos * kOrderSub) / per);
   constexpr int kF = kOrderFine / kOrderQ;            // fine steps within a quarter
   const int q = fine / kF, f = fine - q * kF;
+  if constexpr (PDR_ORDER_WINDOW_MAJOR) {
+    return ((sub * kOrderClasses + (kOrderClasses - 1 - cls)) * kOrderQ + (kOrderQ - 1 - q)) * kF +
+           (kF - 1 - f);
+  }
   return (((kOrderClasses - 1 - cls) * kOrderQ + (kOrderQ - 1 - q)) * kOrderSub + sub) * kF +
          (kF - 1 - f);
 }
