@@ -31,6 +31,7 @@ EXPORTED = (
     "pdr_splat_backward",
     "pdr_splat_bin",
     "pdr_splat_check",
+    "pdr_splat_status_async",
     "pdr_splat_status_string",
     "pdr_splat_timing",
     "pdr_splat_timing_read",
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.pdr_splat_bin.restype = i
         L.pdr_splat_check.argtypes = [vp, vp, ctypes.POINTER(ll)]
         L.pdr_splat_check.restype = i
+        L.pdr_splat_status_async.argtypes = [vp, vp, vp]
+        L.pdr_splat_status_async.restype = i
         L.pdr_splat_status_string.argtypes = [i]
         L.pdr_splat_status_string.restype = ctypes.c_char_p
         L.pdr_splat_timing.argtypes = [i]
@@ -200,6 +203,11 @@ def pdr_splat_check(workspace, stream):
     n = ctypes.c_longlong(0)
     rc = lib().pdr_splat_check(workspace, stream, ctypes.byref(n))
     return rc, n.value
+
+
+def pdr_splat_status_async(workspace, out, stream):
+    """Enqueue the status report of the last call into out (two int64)."""
+    return _raise(lib().pdr_splat_status_async(workspace, out, stream), "pdr_splat_status_async")
 
 
 def pdr_splat_timing(enable: bool) -> bool:

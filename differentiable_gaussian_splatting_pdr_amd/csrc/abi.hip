@@ -184,6 +184,15 @@ __global__ void k_status_out(const WsHeader *hdr, int *out) {
   if (threadIdx.x == 0) *out = (hdr->status & kStatusOverflow) ? PDR_ERR_OVERFLOW : PDR_OK;
 }
 
+// What pdr_splat_check reports, as two integers written in stream order:
+// the pdr_status of the last call and the pair total of its binning.
+__global__ void k_status_pair(const WsHeader *hdr, long long *out) {
+  if (threadIdx.x != 0) return;
+  const int s = hdr->status;
+  out[0] = (s & kStatusOverflow) ? PDR_ERR_OVERFLOW : (s & kStatusStale) ? PDR_ERR_STALE : PDR_OK;
+  out[1] = hdr->total;
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,6 +361,14 @@ int pdr_splat_check(void *workspace, void *stream, long long *pairs_needed) {
   if (h.status & kStatusOverflow) return PDR_ERR_OVERFLOW;
   if (h.status & kStatusStale) return PDR_ERR_STALE;
   return PDR_OK;
+}
+
+int pdr_splat_status_async(void *workspace, long long *out, void *stream) {
+  if (!workspace || !out || ((uintptr_t)out & 7u) != 0) return PDR_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace & 255u) != 0) return PDR_ERR_WORKSPACE;
+  hipLaunchKernelGGL(k_status_pair, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const WsHeader *)workspace, out);
+  return hip_status(hipGetLastError());
 }
 
 long long pdr_loss_workspace_bytes(int B, int H, int W, int C) {

@@ -262,9 +262,11 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
   int f, t;
-  if (hdr->status & kStatusOverflow) return;  // (the order is only complete without overflow)
-  if (order ? !ordered_tile(blockIdx.x, nT, B, order, &f, &t)
-            : !xcd_frame_item(blockIdx.x, nT, B, &f, &t))
+  // Lists that overflowed are incomplete, and so is the tile order: every
+  // pixel of such a call is set to NaN, tiles taken in launch order.
+  const bool ovf = (hdr->status & kStatusOverflow) != 0;
+  if ((order && !ovf) ? !ordered_tile(blockIdx.x, nT, B, order, &f, &t)
+                      : !xcd_frame_item(blockIdx.x, nT, B, &f, &t))
     return;
   __shared__ Entry<CP> s[WL::kBatch];
   __shared__ ThinX sx[WL::kBatch];
@@ -285,10 +287,13 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
 #pragma unroll
     for (int i = 0; i < UX; ++i)
 #pragma unroll
-      for (int c = 0; c < CP; ++c) acc[j][i][c] = 0.f;
+      for (int c = 0; c < CP; ++c) acc[j][i][c] = ovf ? __builtin_nanf("") : 0.f;
 
-  const int beg = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t]);
-  const int end = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t + 1]);
+  int beg = 0, end = 0;
+  if (!ovf) {
+    beg = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t]);
+    end = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t + 1]);
+  }
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
@@ -508,7 +513,21 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
   constexpr int K = CP + 5;
   constexpr int KP = Pow2Up<K>::value;
   int f, t;
-  if (hdr->status & (kStatusOverflow | kStatusStale)) return;
+  if (hdr->status & (kStatusOverflow | kStatusStale)) {
+    // Binning that overflowed, or lists that are not this call's: no lists
+    // to walk.  The finalisation sets dL/dparams to NaN; the pixel branch's
+    // gradient slice (concat) is set to NaN here, tiles in launch order.
+    if (iv.xout && xcd_frame_item(blockIdx.x, nT, B, &f, &t)) {
+      const int px0 = (t % nTx) * kTileW, py0 = (t / nTx) * kTileH;
+      for (int k = threadIdx.x; k < kTileW * kTileH; k += WL::kThreads) {
+        const int px = px0 + k % kTileW, py = py0 + k / kTileW;
+        if (px >= W || py >= H) continue;
+        float *xo = iv.xout + (((size_t)f * H + py) * W + px) * (size_t)iv.Cp;
+        for (int c = 0; c < iv.Cp; ++c) xo[c] = __builtin_nanf("");
+      }
+    }
+    return;
+  }
   if (order ? !ordered_tile(blockIdx.x, nT, B, order, &f, &t)
             : !xcd_frame_item(blockIdx.x, nT, B, &f, &t))
     return;
@@ -696,14 +715,17 @@ __global__ __launch_bounds__(256) void k_finalize(const float *__restrict__ para
                                                   int fmt, int H, int W, double k2) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= BN) return;
-  if (hdr->status & (kStatusOverflow | kStatusStale)) return;
+  const int P = 5 + C;
+  float *o = grad + i * P;
+  if (hdr->status & (kStatusOverflow | kStatusStale)) {   // no valid sums: NaN
+    for (int c = 0; c < P; ++c) o[c] = __builtin_nanf("");
+    return;
+  }
   const uint2 bx = boxes[i];
   const int x0 = (int)(bx.x & 0xFFFFu), x1 = (int)(bx.x >> 16);
   const int y0 = (int)(bx.y & 0xFFFFu), y1 = (int)(bx.y >> 16);
   if (x0 > x1 || y0 > y1) return;
-  const int P = 5 + C;
   const float *g = params + i * P;
-  float *o = grad + i * P;
   double sn, cs;
   sincos((double)g[4], &sn, &cs);
   const double s1 = g[2], s2 = g[3];

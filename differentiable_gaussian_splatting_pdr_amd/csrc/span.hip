@@ -87,7 +87,9 @@ __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
   __shared__ float s_sum[kSpanWaves][KP];
   int f, item;
   if (!xcd_frame_item(blockIdx.x, items, B, &f, &item)) return;
-  if (hdr->status & (kStatusOverflow | kStatusStale)) return;
+  // binning that overflowed, or records that are not this call's: every
+  // gradient of the call is set to NaN
+  const bool bad = (hdr->status & (kStatusOverflow | kStatusStale)) != 0;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int P = 5 + C;
@@ -100,10 +102,14 @@ __global__ __launch_bounds__(kSpanThreads) void k_backward_span(
     const int n = item * kSpanPerBlock + j * kSpanWaves + wv;
     if (n >= N) break;
     const size_t gi = (size_t)f * N + n;
+    float *out = grad + gi * P;
+    if (bad) {
+      for (int c = lane; c < P; c += kWave) out[c] = __builtin_nanf("");
+      continue;
+    }
     const GRec r = recs[gi];
     const int x0 = (int)(r.bx & 0xFFFFu), x1 = (int)(r.bx >> 16);
     const int y0 = (int)(r.by & 0xFFFFu), y1 = (int)(r.by >> 16);
-    float *out = grad + gi * P;
     if (x0 > x1 || y0 > y1) {   // culled or off-screen: zero gradient
       for (int c = lane; c < P; c += kWave) out[c] = 0.f;
       continue;

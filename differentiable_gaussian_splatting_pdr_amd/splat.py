@@ -10,6 +10,8 @@ ROCm device, be float32 and contiguous:
 """
 from __future__ import annotations
 
+import threading
+
 import torch
 
 from . import _lib
@@ -188,29 +190,272 @@ def bin_lists(params: torch.Tensor, H: int, W: int, radius: float = 3.0):
     raise _lib.PdrError(_lib.PDR_ERR_OVERFLOW, "pdr_splat_bin")
 
 
+# ----------------------------------------------------- persistent workspaces
+
+class _Entry:
+    """One persistent workspace: its buffer, pair capacity, the call whose
+    binning it holds, and the status reports still in flight."""
+
+    def __init__(self, ws: Workspace, cap: int, key):
+        self.ws = ws
+        self.cap = cap
+        self.key = key        # (B, N, H, W, C)
+        self.gen = 0          # ids handed to calls that bin into this workspace
+        self.holder = None    # id of the call whose binning the workspace holds
+        self.pending = []     # (host int64[2], event, call id), oldest first
+        self.free = []        # pinned int64[2] host buffers for reuse
+        self.dev_status = torch.empty(2, dtype=torch.int64, device=ws.device)
+
+
+class Renderer:
+    """Persistent, size-keyed workspaces for repeated renders.
+
+    A training loop renders problems of the same sizes every step; the
+    one-shot :func:`forward` synchronises after each call to check the list
+    capacity.  A Renderer instead keeps one workspace per (device, stream, B,
+    N, H, W, C) and synchronises (pdr_splat_check) only when it creates or
+    grows a workspace: the first call of a size binds with a checked forward
+    and sizes the workspace to `headroom` times the pairs it needed.  Later
+    calls enqueue a status report (pdr_splat_status_async, copied to pinned
+    host memory) and read it once the GPU has passed it, without waiting.  A
+    report of overflow -- the Gaussians grew past the headroom -- means that
+    call's outputs were NaN: the workspace grows to fit and the next call on
+    the Renderer that sees the report (or :meth:`flush`) raises
+    :class:`_lib.PdrError` with PDR_ERR_OVERFLOW, so the loop can repeat the
+    step.
+
+    The backward of a render reuses the forward's binning when the workspace
+    still holds it, and bins again otherwise (another render of the same
+    sizes came in between).  Calls that share one Renderer on one stream are
+    ordered; a Renderer is safe to use from several threads (autograd runs
+    backward on its own thread).  At most `max_entries` sizes are kept (least
+    recently used first out); `max_pending` status reports may be in flight
+    per workspace before the oldest is waited for.
+    """
+
+    def __init__(self, headroom: float = 1.25, max_entries: int = 8, max_pending: int = 64):
+        if not headroom >= 1.0:
+            raise ValueError("headroom must be >= 1")
+        self.headroom = float(headroom)
+        self.max_entries = int(max_entries)
+        self.max_pending = int(max_pending)
+        self._entries = {}    # key -> _Entry, least recently used first
+        self._lock = threading.RLock()
+        self._overflowed = []  # (sizes, pairs needed, new capacity) not yet raised
+        self._retired = []     # evicted entries with reports in flight
+
+    # -- status reports
+    def _track(self, e: _Entry, gen: int, st: int):
+        _lib.pdr_splat_status_async(e.ws.ptr, e.dev_status.data_ptr(), st)
+        if len(e.pending) >= self.max_pending:
+            self._read(e, e.pending[0], wait=True)
+        host = e.free.pop() if e.free else torch.empty(2, dtype=torch.int64, pin_memory=True)
+        host.copy_(e.dev_status, non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream(e.ws.device))
+        e.pending.append((host, ev, gen))
+
+    def _read(self, e: _Entry, item, wait: bool) -> bool:
+        host, ev, gen = item
+        if wait:
+            ev.synchronize()
+        elif not ev.query():
+            return False
+        e.pending.remove(item)
+        rc, need = int(host[0]), int(host[1])
+        e.free.append(host)
+        if rc == _lib.PDR_ERR_OVERFLOW:
+            self._grow(e, need)
+            self._overflowed.append((e.key, need, e.cap))
+        elif rc != _lib.PDR_OK:
+            raise _lib.PdrError(rc, "Renderer")
+        return True
+
+    def _drain(self, e: _Entry | None, wait: bool = False):
+        for x in ([e] if e is not None else []) + self._retired:
+            for item in list(x.pending):
+                if not self._read(x, item, wait):
+                    break   # reports complete in stream order
+        self._retired = [x for x in self._retired if x.pending]
+        if self._overflowed:
+            (B, N, H, W, C), need, cap = self._overflowed.pop(0)
+            raise _lib.PdrError(
+                _lib.PDR_ERR_OVERFLOW,
+                "render of %d x %d Gaussians on %dx%dx%d frames needed %d (tile, Gaussian) pairs; "
+                "that call's outputs are NaN and the workspace now holds %d pairs, repeat the step"
+                % (B, N, H, W, C, need, cap))
+
+    def _grow(self, e: _Entry, need: int):
+        B, N, H, W, C = e.key
+        cap = min(max(int(need * self.headroom) + 1024, e.cap), 0x7FFFFFFF)
+        if cap > e.cap:
+            e.ws.buf = torch.empty(Workspace.bytes_for(B, N, H, W, C, cap), dtype=torch.uint8,
+                                   device=e.ws.device)
+            e.cap = cap
+            e.holder = None      # a fresh buffer holds no binning
+            e.dev_status = torch.empty(2, dtype=torch.int64, device=e.ws.device)
+
+    def flush(self):
+        """Wait for every status report in flight; raises as a later call
+        would if one of them overflowed."""
+        with self._lock:
+            for e in list(self._entries.values()):
+                self._drain(e, wait=True)
+            self._drain(None, wait=True)
+
+    # -- workspaces
+    def _entry(self, params, H, W, radius, launch):
+        """The workspace for this problem, running `launch(ws)` in it: checked
+        when the workspace is new, else with a status report.  Returns the
+        entry and the id of the call."""
+        B, N, C = _check_params(params)
+        dev = params.device
+        st = _stream(dev)
+        key = (B, N, H, W, C)
+        full = (dev.index, st) + key
+        e = self._entries.pop(full, None)
+        if e is None:
+            cap = _initial_pairs(B, N, H, W)
+            ws = Workspace(dev, Workspace.bytes_for(B, N, H, W, C, cap))
+            for _ in range(2):
+                launch(ws)
+                rc, need = _lib.pdr_splat_check(ws.ptr, st)
+                if rc == _lib.PDR_OK:
+                    break
+                if rc != _lib.PDR_ERR_OVERFLOW:
+                    raise _lib.PdrError(rc, "Renderer")
+                cap = need
+                ws.ensure(Workspace.bytes_for(B, N, H, W, C, cap))
+            else:
+                raise _lib.PdrError(_lib.PDR_ERR_OVERFLOW, "Renderer")
+            e = _Entry(ws, cap, key)
+            e.gen = 1
+            e.holder = 1
+            if need * self.headroom + 1024 > e.cap:
+                self._grow(e, need)           # the binning just made is gone
+        else:
+            self._entries[full] = e
+            self._drain(e)
+            launch(e.ws)
+            e.gen += 1
+            e.holder = e.gen
+            self._track(e, e.gen, st)
+        self._entries[full] = e
+        while len(self._entries) > self.max_entries:
+            old = self._entries.pop(next(iter(self._entries)))
+            if old.pending:
+                self._retired.append(old)    # its reports are still read
+        return e, e.gen
+
+    def forward(self, params, H: int, W: int, radius: float = 3.0):
+        """image [B, H, W, C] (fp32); returns (image, entry, call id)."""
+        B, N, C = _check_params(params)
+        image = torch.empty((B, H, W, C), dtype=torch.float32, device=params.device)
+
+        def launch(ws):
+            _lib.pdr_splat_forward(params.data_ptr(), image.data_ptr(), B, N, H, W, C, radius,
+                                   ws.ptr, ws.nbytes, _stream(params.device))
+        with self._lock:
+            e, gen = self._entry(params, H, W, radius, launch)
+        return image, e, gen
+
+    def forward_concat(self, params, pixel, H: int, W: int, radius: float = 3.0):
+        """[pixel | render(params)] [B, H, W, Cp + C]; returns (out, entry, call id)."""
+        B, N, C = _check_params(params)
+        if pixel.dim() != 4 or pixel.shape[:3] != (B, H, W) or pixel.dtype != torch.float32:
+            raise ValueError("pixel must be float32 [B, H, W, Cp]")
+        pixel = pixel.contiguous()
+        Cp = pixel.shape[3]
+        out = torch.empty((B, H, W, Cp + C), dtype=torch.float32, device=params.device)
+
+        def launch(ws):
+            _lib.pdr_splat_forward_concat(params.data_ptr(), pixel.data_ptr(), Cp, out.data_ptr(),
+                                          B, N, H, W, C, radius, ws.ptr, ws.nbytes,
+                                          _stream(params.device))
+        with self._lock:
+            e, gen = self._entry(params, H, W, radius, launch)
+        return out, e, gen
+
+    def _backward(self, e: _Entry, gen: int, params, launch):
+        with self._lock:
+            self._drain(e)
+            reuse = e.holder == gen
+            if not reuse:            # binning again replaces what the workspace held
+                e.gen += 1
+                e.holder = e.gen
+            launch(e.ws, reuse)
+            if not reuse:
+                self._track(e, e.holder, _stream(params.device))
+
+    def backward(self, e: _Entry, gen: int, params, grad_image, H: int, W: int,
+                 radius: float = 3.0):
+        """dL/dparams of the render `gen` from dL/dimage (fp32)."""
+        B, N, C = _check_params(params)
+        grad_image = grad_image.contiguous()
+        if grad_image.shape != (B, H, W, C) or grad_image.dtype != torch.float32:
+            raise ValueError("grad_image must be float32 [B, H, W, C]")
+        grad_params = torch.empty_like(params)
+
+        def launch(ws, reuse):
+            _lib.pdr_splat_backward(params.data_ptr(), grad_image.data_ptr(),
+                                    grad_params.data_ptr(), B, N, H, W, C, radius, ws.ptr,
+                                    ws.nbytes, int(reuse), _stream(params.device))
+        self._backward(e, gen, params, launch)
+        return grad_params
+
+    def backward_concat(self, e: _Entry, gen: int, params, grad_out, Cp: int, H: int, W: int,
+                        radius: float = 3.0, want_pixel_grad: bool = True):
+        """(dL/dparams, dL/dpixel or None) of the concat render `gen`."""
+        B, N, C = _check_params(params)
+        grad_out = grad_out.contiguous()
+        if grad_out.shape != (B, H, W, Cp + C) or grad_out.dtype != torch.float32:
+            raise ValueError("grad_out must be float32 [B, H, W, Cp + C]")
+        grad_params = torch.empty_like(params)
+        grad_pixel = (torch.empty((B, H, W, Cp), dtype=torch.float32, device=params.device)
+                      if want_pixel_grad and Cp > 0 else None)
+
+        def launch(ws, reuse):
+            _lib.pdr_splat_backward_concat(
+                params.data_ptr(), grad_out.data_ptr(), Cp, grad_params.data_ptr(),
+                grad_pixel.data_ptr() if grad_pixel is not None else None, B, N, H, W, C, radius,
+                ws.ptr, ws.nbytes, int(reuse), _stream(params.device))
+        self._backward(e, gen, params, launch)
+        return grad_params, grad_pixel
+
+
+_renderer = Renderer()
+
+
+def default_renderer() -> Renderer:
+    """The Renderer behind :func:`render` and :func:`render_concat`."""
+    return _renderer
+
+
 class SplatRender(torch.autograd.Function):
     """image = render(params); backward reuses the forward's binning."""
 
     @staticmethod
-    def forward(ctx, params, H, W, radius):
+    def forward(ctx, params, H, W, radius, renderer):
         params = params.contiguous()
-        image, ws = forward(params, H, W, radius)
+        r = renderer or _renderer
+        image, e, gen = r.forward(params, H, W, radius)
         ctx.save_for_backward(params)
-        ctx.meta = (H, W, radius, ws)
+        ctx.meta = (H, W, radius, r, e, gen)
         return image
 
     @staticmethod
     def backward(ctx, grad_image):
         (params,) = ctx.saved_tensors
-        H, W, radius, ws = ctx.meta
-        g = backward(params, grad_image.contiguous(), H, W, radius, workspace=ws,
-                     reuse_binning=True)
-        return g, None, None, None
+        H, W, radius, r, e, gen = ctx.meta
+        g = r.backward(e, gen, params, grad_image, H, W, radius)
+        return g, None, None, None, None
 
 
-def render(params: torch.Tensor, H: int, W: int, radius: float = 3.0) -> torch.Tensor:
-    """Differentiable render of [B, N, 5 + C] Gaussians to [B, H, W, C]."""
-    return SplatRender.apply(params, H, W, radius)
+def render(params: torch.Tensor, H: int, W: int, radius: float = 3.0,
+           renderer: Renderer | None = None) -> torch.Tensor:
+    """Differentiable render of [B, N, 5 + C] Gaussians to [B, H, W, C]
+    through a Renderer's persistent workspaces (the module's by default)."""
+    return SplatRender.apply(params, H, W, radius, renderer)
 
 
 def l1_ssim_loss(image: torch.Tensor, target: torch.Tensor, lam: float = 0.2,
@@ -314,24 +559,26 @@ class SplatRenderConcat(torch.autograd.Function):
     """out = [pixel | render(params)]; backward reuses the forward's binning."""
 
     @staticmethod
-    def forward(ctx, params, pixel, H, W, radius):
+    def forward(ctx, params, pixel, H, W, radius, renderer):
         params = params.contiguous()
-        out, ws = forward_concat(params, pixel, H, W, radius)
+        r = renderer or _renderer
+        out, e, gen = r.forward_concat(params, pixel, H, W, radius)
         ctx.save_for_backward(params)
-        ctx.meta = (H, W, radius, ws, pixel.shape[3])
+        ctx.meta = (H, W, radius, r, e, gen, pixel.shape[3])
         return out
 
     @staticmethod
     def backward(ctx, grad_out):
         (params,) = ctx.saved_tensors
-        H, W, radius, ws, Cp = ctx.meta
-        gp, gx = backward_concat(params, grad_out.contiguous(), Cp, H, W, radius, workspace=ws,
-                                 reuse_binning=True, want_pixel_grad=ctx.needs_input_grad[1])
-        return gp, gx, None, None, None
+        H, W, radius, r, e, gen, Cp = ctx.meta
+        gp, gx = r.backward_concat(e, gen, params, grad_out, Cp, H, W, radius,
+                                   want_pixel_grad=ctx.needs_input_grad[1])
+        return gp, gx, None, None, None, None
 
 
-def render_concat(params, pixel, H: int, W: int, radius: float = 3.0):
-    return SplatRenderConcat.apply(params, pixel, H, W, radius)
+def render_concat(params, pixel, H: int, W: int, radius: float = 3.0,
+                  renderer: Renderer | None = None):
+    return SplatRenderConcat.apply(params, pixel, H, W, radius, renderer)
 
 
 # ------------------------------------------------------ grid and activations

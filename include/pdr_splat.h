@@ -39,7 +39,10 @@
  *    is returned and nothing runs.  Launch failures return PDR_ERR_HIP.
  *  - Data-dependent failures (list capacity overflow, a stale workspace on
  *    reuse) are raised on the device into the workspace header and reported
- *    by pdr_splat_check; outputs of such a call are undefined.
+ *    by pdr_splat_check or pdr_splat_status_async.  Every element of the
+ *    outputs of such a call is NaN (image, grad_params, grad_pixel); the
+ *    lists and counts of pdr_splat_bin and pdr_splat_count_support are then
+ *    undefined.
  *  - Reentrant: concurrent calls need distinct workspaces.
  */
 #ifndef PDR_SPLAT_H
@@ -139,6 +142,18 @@ int pdr_splat_count_support(const float *params, int B, int N, int H, int W, int
  * PDR_ERR_HIP).  *pairs_needed (may be NULL) receives the pair total of the
  * last binning. */
 int pdr_splat_check(void *workspace, void *stream, long long *pairs_needed);
+
+/* The report of pdr_splat_check without synchronising: enqueues on `stream`
+ * a one-thread kernel that writes out[0] = the pdr_status of the last call
+ * on `workspace` (PDR_OK, PDR_ERR_OVERFLOW or PDR_ERR_STALE) and out[1] =
+ * the pair total of its binning.  `out` (two int64, 8-byte aligned) is a
+ * device pointer; the caller copies it to host memory asynchronously
+ * (hipMemcpyAsync into pinned memory, then an event) and reads it once the
+ * event has completed.  Lets a training loop check capacity a step late
+ * instead of stalling every step.  Returns PDR_ERR_INVALID_ARG for a null or misaligned `out`,
+ * PDR_ERR_WORKSPACE for a misaligned workspace; the workspace must have
+ * served a call before (its header is otherwise unset). */
+int pdr_splat_status_async(void *workspace, long long *out, void *stream);
 
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc: the forward
