@@ -45,7 +45,7 @@ def kernel_bytes(B, N, H, W, C, pairs_tiles, T):
     return {
         "preprocess": BN * P * 4 + BN * 40,
         "bin_count": BN * 8 + B * nT * 4,
-        "scan": 2 * B * nT * 4,
+        "scan": None,   # the group totals: a few KB whose count depends on the binning plan
         "bin_write": BN * 8 + B * nT * 4 + pairs_tiles * 4,
         "forward_raster": pairs_tiles * 4 + BN * (32 + C * 4) + img,
         "zero_verify": BN * P * 4,
@@ -155,6 +155,166 @@ def backward_algo_leg(args, _lib, torch, B, N, H, W, C, params, grad_image, grad
     return out
 
 
+# Kernel classes of the per-kernel timing, by kernel name prefix (rocprofv3
+# names kernels "pdr::k_...(args)").
+KERNEL_CLASSES = (("k_preprocess", "preprocess"), ("k_rows<", "bin_count"),
+                  ("k_rowscan", "bin_count"), ("k_rowstart", "bin_count"),
+                  ("k_bin<false", "bin_count"), ("k_count_scan", "scan"),
+                  ("k_bin<true", "bin_write"), ("k_forward<", "forward_raster"),
+                  ("k_zero_verify", "zero_verify"), ("k_backward<", "backward_raster"),
+                  ("k_finalize", "finalize"))
+CSRC = "differentiable_gaussian_splatting_pdr_amd/csrc"
+
+
+def kernel_sources():
+    """Every file the library is built from: a summary of counters or
+    durations is only valid for the build it was taken on."""
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(os.path.join(ROOT, CSRC))
+                   if f.endswith((".hip", ".hpp")))
+    return files + ["include/pdr_splat.h", "differentiable_gaussian_splatting_pdr_amd/build.py"]
+
+
+def short_kernel_name(name):
+    import re
+    m = re.search(r"\b(k_\w+(<[^(]*>)?)", name)
+    return m.group(1) if m else name.split("(")[0][:60]
+
+
+def kernel_class(short):
+    for prefix, cls in KERNEL_CLASSES:
+        if short.startswith(prefix):
+            return cls
+    return None
+
+
+def sizes_tag(wl):
+    return "%dx%dx%dx%d_n%d" % (wl.B, wl.H, wl.W, wl.C, wl.N)
+
+
+def workload_text(wl, radius):
+    return "%d frames of %dx%dx%d, N=%d Gaussians/frame, %g-sigma truncation" % (
+        wl.B, wl.H, wl.W, wl.C, wl.N, radius)
+
+
+def _find_csv(d, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit("no *%s under %s" % (suffix, d))
+    return hits
+
+
+def summarize(args):
+    """Summaries of rocprofv3 output for profiles/ (host only)."""
+    import csv
+    import statistics
+    from differentiable_gaussian_splatting_pdr_amd import workloads
+    wl = workloads.WORKLOADS[args.workload]
+    tag = sizes_tag(wl)
+    srcs = kernel_sources()
+    if args.summarize_trace:
+        rows = []
+        for f in _find_csv(args.summarize_trace, "kernel_trace.csv"):
+            rows += list(csv.DictReader(open(f)))
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        per = {}
+        for r in rows:
+            k = short_kernel_name(r["Kernel_Name"])
+            per.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        last = args.profile_loop
+        kernels, classes = {}, {}
+        for k, v in per.items():
+            tail = v[-last:] if last else v
+            kernels[k] = {"calls": len(v), "avg_us_all": round(statistics.mean(v), 2),
+                          "min_us": round(min(v), 2), "max_us": round(max(v), 2),
+                          "avg_us_last": round(statistics.mean(tail), 2), "last": len(tail),
+                          "class": kernel_class(k)}
+            if kernel_class(k) and len(v) >= last:
+                c = kernel_class(k)
+                classes[c] = round(classes.get(c, 0.0) + statistics.mean(tail), 2)
+        stats = []
+        for f in _find_csv(args.summarize_trace, "kernel_stats.csv"):
+            stats += list(csv.DictReader(open(f)))
+        out = {"workload": workload_text(wl, args.radius), "command": args.command,
+               "warmup_steps": args.warmup, "profiled_steps": last, "sources": srcs,
+               "source_digest": source_digest(srcs), "kernels": kernels,
+               "class_avg_us_last": classes,
+               "note": "avg_us_last: mean over each kernel's last profiled_steps dispatches "
+                       "(steady clocks); avg_us_all: over every dispatch of the run, the "
+                       "figure of rocprofv3 --stats"}
+        jpath = os.path.join(ROOT, "profiles", "kernel_trace_%s.json" % tag)
+        with open(jpath, "w") as fh:
+            json.dump(out, fh, indent=1)
+            fh.write("\n")
+        md = ["# Kernel trace: %s, MI355X" % workload_text(wl, args.radius), "",
+              "Command (from /tmp with TMPDIR=/tmp; `<repo>` is the repository root):", "",
+              "    " + args.command, "",
+              "Summarised by `python3 bench.py --summarize-trace <dir> --warmup %d "
+              "--profile-loop %d --workload %d`.  The program runs one checked step, %d "
+              "warm-up steps and %d profiled steps (forward + backward reusing the binning)."
+              % (args.warmup, last, args.workload, args.warmup, last), "",
+              "rocprofv3 `--stats` (every dispatch of the run):", "",
+              "| kernel | calls | avg us | min us | max us | % GPU time |", "|---|---|---|---|---|---|"]
+        for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+            md.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f |" % (
+                short_kernel_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        md += ["", "Steady state, mean over each kernel's last %d dispatches of the trace:" % last,
+               "", "| kernel | class | avg us (last %d) | avg us (all) |" % last, "|---|---|---|---|"]
+        for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["avg_us_last"]):
+            if v["calls"] >= last:
+                md.append("| `%s` | %s | %.1f | %.1f |" % (k, v["class"], v["avg_us_last"],
+                                                            v["avg_us_all"]))
+        md += ["", "bench.py reads the `class_avg_us_last` figures from `kernel_trace_%s.json` "
+               "(when its source digest matches the build) and reports the roofline of the "
+               "dominant kernel from both its live HIP-event timing and this trace." % tag, ""]
+        with open(os.path.join(ROOT, "profiles", "kernel_trace_%s.md" % tag), "w") as fh:
+            fh.write("\n".join(md))
+        print(json.dumps({"written": [os.path.relpath(jpath, ROOT)], "classes": classes}))
+    if args.summarize_pmc:
+        vals = {}
+        for d, counter in zip(args.summarize_pmc, ("FETCH_SIZE", "WRITE_SIZE")):
+            for f in _find_csv(d, "counter_collection.csv"):
+                for r in csv.DictReader(open(f)):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    k = short_kernel_name(r["Kernel_Name"])
+                    vals.setdefault((counter, k), []).append(float(r["Counter_Value"]))
+        if not args.calib_copy_mb:
+            raise SystemExit("--summarize-pmc needs --calib-copy-mb (the reference copy's size)")
+        true_kib = args.calib_copy_mb * 1024.0
+        out = {"kernel": args.kernel, "workload": workload_text(wl, args.radius),
+               "sources": srcs, "source_digest": source_digest(srcs),
+               "commands": args.command.split(" && ") if args.command else []}
+        total = 0.0
+        for counter, key in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            copies = [max(v) for (c, k), v in vals.items() if c == counter and "copyBuffer" in k]
+            if not copies:
+                raise SystemExit("no reference copy in the %s run" % counter)
+            scale = true_kib / max(copies)
+            ks = [(k, v) for (c, k), v in vals.items()
+                  if c == counter and kernel_class(k) == args.kernel]
+            if len(ks) != 1:
+                raise SystemExit("kernel class %s: %d kernels in the %s run" % (
+                    args.kernel, len(ks), counter))
+            k, v = ks[0]
+            b = statistics.median(v) * 1024.0 * scale
+            out[key + "_bytes"] = b
+            out[key + "_scale"] = scale
+            out["kernel_name"] = k
+            total += b
+        out["bytes_per_launch"] = total
+        out["scaling_rule"] = ("median KiB per dispatch x 1024, times the ratio of a %d MiB "
+                               "copy's true bytes to what the same counter reads for it"
+                               % args.calib_copy_mb)
+        path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (args.kernel, tag))
+        with open(path, "w") as fh:
+            json.dump(out, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps({"written": os.path.relpath(path, ROOT),
+                          "bytes_per_launch": total}))
+
+
 def source_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -206,8 +366,10 @@ def cpu_baseline_leg(params, grad, wl, radius, budget_s, want_count=True):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first: the rasters' launch durations settle over about "
+                         "the first 40 launches of a run while the clocks ramp")
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--radius", type=float, default=3.0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -221,7 +383,23 @@ def main():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="with --profile-loop: also run one device-to-device copy of this many "
                          "MiB, the reference kernel for scaling HBM byte counters")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="no GPU: write profiles/kernel_trace_<sizes>.{json,md} from the "
+                         "rocprofv3 --kernel-trace --stats output in DIR of a --profile-loop run "
+                         "(pass the same --workload, --warmup and --profile-loop)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: write profiles/traffic_<kernel>_<sizes>.json from two "
+                         "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a --profile-loop run "
+                         "with --calib-copy-mb (pass the same --calib-copy-mb)")
+    ap.add_argument("--kernel", default="backward_raster",
+                    help="with --summarize-pmc: the kernel class to summarise")
+    ap.add_argument("--command", default="",
+                    help="with --summarize-*: the rocprofv3 command(s) that made the input, "
+                         "recorded in the summary ('<repo>' for the repository root)")
     args = ap.parse_args()
+    if args.summarize_trace or args.summarize_pmc:
+        summarize(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(frames are independent; see the design notes on sharding)", file=sys.stderr)
@@ -390,8 +568,9 @@ def main():
         if cnt == 0:
             continue
         avg = tot_ms / cnt
-        row = {"avg_ms": round(avg, 5), "launches_per_step": cnt // args.steps,
-               "alg_GBps": round(kb[name] / (avg * 1e-3) / 1e9, 1)}
+        row = {"avg_ms": round(avg, 5), "launches_per_step": cnt // args.steps}
+        if kb.get(name) is not None:
+            row["alg_GBps"] = round(kb[name] / (avg * 1e-3) / 1e9, 1)
         if support_pairs is not None and name in ("forward_raster", "backward_raster"):
             fl = support_pairs * (f_fwd if name == "forward_raster" else f_bwd)
             row["alg_TFLOPs"] = round(fl / (avg * 1e-3) / 1e12, 3)
@@ -402,17 +581,36 @@ def main():
         fl = support_pairs * (f_fwd if dom == "forward_raster" else f_bwd)
         avg = kernels[dom]["avg_ms"] * 1e-3
         ach = fl / avg / 1e12
-        traffic = None
-        tpath = os.path.join(ROOT, "profiles", "traffic_%s_%dx%dx%dx%d_n%d.json" % (dom, B, H, W, C, N))
-        if os.path.exists(tpath):
-            with open(tpath) as fh:
+        tag = sizes_tag(wl)
+
+        def committed(name):
+            # a profiles/ summary, if it was taken on the sources built here
+            path = os.path.join(ROOT, "profiles", name)
+            if not os.path.exists(path):
+                return None, path
+            with open(path) as fh:
                 t = json.load(fh)
-            if t.get("source_digest") == source_digest(t.get("sources", [])):
-                traffic = t.get("bytes_per_launch")
+            ok = t.get("sources") == kernel_sources() and \
+                t.get("source_digest") == source_digest(t.get("sources", []))
+            return (t if ok else None), path
+
+        t, tpath = committed("traffic_%s_%s.json" % (dom, tag))
+        traffic = t.get("bytes_per_launch") if t else None
+        t, kpath = committed("kernel_trace_%s.json" % tag)
+        traced = None
+        if t and dom in t.get("class_avg_us_last", {}):
+            tus = t["class_avg_us_last"][dom]
+            tach = fl / (tus * 1e-6) / 1e12
+            traced = {"avg_launch_ms": round(tus * 1e-3, 5), "achieved": round(tach, 3),
+                      "frac": round(tach / FP32_PEAK_TFLOPS, 4),
+                      "profile": os.path.relpath(kpath, ROOT)}
         roofline = {"bound": "alu", "achieved": round(ach, 3), "peak": FP32_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ach / FP32_PEAK_TFLOPS, 4),
                     "traffic": traffic, "kernel": dom,
-                    "flops_per_launch": fl, "avg_launch_ms": kernels[dom]["avg_ms"]}
+                    "flops_per_launch": fl, "avg_launch_ms": kernels[dom]["avg_ms"],
+                    "alg_bytes_per_launch": kb[dom],
+                    "traffic_profile": os.path.relpath(tpath, ROOT) if traffic else None,
+                    "traced": traced}
     value = support_pairs / (ms * 1e-3) if support_pairs is not None else None
     out = {
         "metric": "fwd+bwd Gaussian-pixel evals/s and frames/s at 128x128x3, N=4096; % FP32 peak",

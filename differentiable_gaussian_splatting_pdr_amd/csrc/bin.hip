@@ -916,9 +916,11 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
       hipLaunchKernelGGL(k_count, g2, dim3(kBinThreads), lds2, st, boxes, B, N, nTx, nTy, 1,
                          bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr, (int *)nullptr,
                          cap, hdr, ohist, order, (const int *)rlist, (const int *)fstart, L.cap);
-      hipLaunchKernelGGL(k_count_scan, dim3(9), dim3(kBinThreads), 0, st, gtot,
-                         (long long)B * bg.G, cap, hdr, ohist, (unsigned)(B * nTx * nTy));
     });
+    PDR_TIMED(PDR_K_SCAN, st,
+              hipLaunchKernelGGL(k_count_scan, dim3(9), dim3(kBinThreads), 0, st, gtot,
+                                 (long long)B * bg.G, cap, hdr, ohist,
+                                 (unsigned)(B * nTx * nTy)));
     PDR_TIMED(PDR_K_BIN_WRITE, st,
               hipLaunchKernelGGL(k_write, g2, dim3(kBinThreads), lds2, st, boxes, B, N, nTx, nTy,
                                  1, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, tile_off, list, cap,
@@ -940,9 +942,10 @@ hipError_t launch_binning(const float *params, int B, int N, int H, int W, int C
     hipLaunchKernelGGL(k_count, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy, bg.gh,
                        bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, (int *)nullptr, (int *)nullptr,
                        cap, hdr, ohist, order, (const int *)nullptr, (const int *)nullptr, 0LL);
-    hipLaunchKernelGGL(k_count_scan, dim3(9), dim3(kBinThreads), 0, st, gtot, (long long)B * bg.G,
-                       cap, hdr, ohist, (unsigned)(B * nTx * nTy));
   });
+  PDR_TIMED(PDR_K_SCAN, st,
+            hipLaunchKernelGGL(k_count_scan, dim3(9), dim3(kBinThreads), 0, st, gtot,
+                               (long long)B * bg.G, cap, hdr, ohist, (unsigned)(B * nTx * nTy)));
   PDR_TIMED(PDR_K_BIN_WRITE, st,
             hipLaunchKernelGGL(k_write, grid, dim3(kBinThreads), lds, st, boxes, B, N, nTx, nTy,
                                bg.gh, bg.ncc, bg.cw, bg.G, bg.NC, counts, gtot, tile_off, list, cap,

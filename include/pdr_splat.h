@@ -184,9 +184,11 @@ const char *pdr_splat_status_string(int status);
  * pdr_splat_timing returns the previous state.  pdr_splat_timing_read waits
  * for the recorded events and fills total_ms[k] / launches[k] (arrays of
  * PDR_KERNEL_COUNT, may be NULL) with the accumulated milliseconds and launch
- * counts per kernel class k; reset != 0 clears the accumulators.  The
- * scan of the per-tile counts runs inside the list-writing kernel, so
- * PDR_K_SCAN records no launches. */
+ * counts per kernel class k; reset != 0 clears the accumulators.
+ * PDR_K_BIN_COUNT covers the count pass (with the per-row lists of two-level
+ * binning), PDR_K_SCAN the scan of the group totals and the tile order's
+ * cursors, PDR_K_BIN_WRITE the list-writing pass (which scans the per-tile
+ * counts of its group). */
 enum pdr_kernel_id {
     PDR_K_PREPROCESS = 0, PDR_K_BIN_COUNT = 1, PDR_K_SCAN = 2, PDR_K_BIN_WRITE = 3,
     PDR_K_FORWARD_RASTER = 4, PDR_K_ZERO = 5, PDR_K_BACKWARD_RASTER = 6, PDR_K_FINALIZE = 7,

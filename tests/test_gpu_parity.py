@@ -345,7 +345,7 @@ def test_timing_counts_launches():
     finally:
         _lib.pdr_splat_timing(False)
     assert t["forward_raster"][1] == 1 and t["backward_raster"][1] == 1
-    assert t["bin_count"][1] == 1 and t["bin_write"][1] == 1 and t["scan"][1] == 0
+    assert t["bin_count"][1] == 1 and t["bin_write"][1] == 1 and t["scan"][1] == 1
     assert t["backward_raster"][0] > 0.0
 
 
