@@ -29,7 +29,9 @@ int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
   if (H > kMaxHW || W > kMaxHW || N > kMaxN) return PDR_ERR_INVALID_ARG;
   if ((W + kTileW - 1) / kTileW > kMaxGroupTiles) return PDR_ERR_INVALID_ARG;  // one tile row per bin group
   long long BN = (long long)B * N;
-  if (BN * (5 + C) > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;  // int32 parameter offsets
+  // int32 parameter offsets (by division: the product could exceed 64 bits)
+  if (BN > 0x7fffffffLL / (5 + (long long)C)) return PDR_ERR_INVALID_ARG;
+  // below 2^31 * 2^15 * 2^14 here, as B C < 2^31
   if ((long long)B * H * W * C > (1LL << 46)) return PDR_ERR_INVALID_ARG;
   d->nTx = (W + kTileW - 1) / kTileW;
   d->nTy = (H + kTileH - 1) / kTileH;
@@ -37,6 +39,15 @@ int validate_sizes(int B, int N, int H, int W, int C, Dims *d) {
   d->BT = (long long)B * d->nTx * d->nTy;
   if (d->BT + 1 > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
   d->rp = row_plan(B, N, H, W);
+  return PDR_OK;
+}
+
+// Channels per output pixel of the concat layout (pixel branch + rendered):
+// the row stride of the image kernels is a 32-bit int.
+constexpr long long kMaxOutChannels = 65536;
+int validate_out(int B, int H, int W, int Cp, int C) {
+  if (Cp < 0 || (long long)Cp + C > kMaxOutChannels) return PDR_ERR_INVALID_ARG;
+  if ((long long)B * H * W * (Cp + (long long)C) > (1LL << 46)) return PDR_ERR_INVALID_ARG;
   return PDR_OK;
 }
 
@@ -88,7 +99,7 @@ int forward_impl(const float *params, const float *pixel, int Cp, void *image, i
   if (fmt != PDR_FMT_F32 && fmt != PDR_FMT_F16 && fmt != PDR_FMT_BF16) return PDR_ERR_INVALID_ARG;
   int rc = validate_sizes(B, N, H, W, C, &d);
   if (rc == PDR_OK) rc = validate_radius(radius);
-  if (rc == PDR_OK && (long long)B * H * W * (Cp + (long long)C) > (1LL << 46)) rc = PDR_ERR_INVALID_ARG;
+  if (rc == PDR_OK) rc = validate_out(B, H, W, Cp, C);
   if (rc == PDR_OK) rc = layout_for(d, workspace, workspace_bytes, &L);
   if (rc != PDR_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
@@ -111,7 +122,7 @@ int backward_impl(const float *params, const void *grad_image, int Cp, float *gr
   if (fmt != PDR_FMT_F32 && fmt != PDR_FMT_F16 && fmt != PDR_FMT_BF16) return PDR_ERR_INVALID_ARG;
   int rc = validate_sizes(B, N, H, W, C, &d);
   if (rc == PDR_OK) rc = validate_radius(radius);
-  if (rc == PDR_OK && (long long)B * H * W * (Cp + (long long)C) > (1LL << 46)) rc = PDR_ERR_INVALID_ARG;
+  if (rc == PDR_OK) rc = validate_out(B, H, W, Cp, C);
   if (rc != PDR_OK) return rc;
   if (algo != PDR_BWD_AUTO && algo != PDR_BWD_TILE && algo != PDR_BWD_SPAN) return PDR_ERR_INVALID_ARG;
   const bool span_ok = Cp == 0 && span_backward_supported(H, W, C);
@@ -146,7 +157,7 @@ int validate_grid(int B, int gx, int gy, int H, int W, int C) {
   if (H > kMaxHW || W > kMaxHW) return PDR_ERR_INVALID_ARG;
   const long long N = (long long)gx * gy;
   if (N > kMaxN) return PDR_ERR_INVALID_ARG;
-  if ((long long)B * N * (5 + (long long)C) > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
+  if ((long long)B * N > 0x7fffffffLL / (5 + (long long)C)) return PDR_ERR_INVALID_ARG;
   return PDR_OK;
 }
 
@@ -373,8 +384,9 @@ int pdr_splat_status_async(void *workspace, long long *out, void *stream) {
 
 long long pdr_loss_workspace_bytes(int B, int H, int W, int C) {
   if (B < 1 || H < 1 || W < 1 || C < 1) return PDR_ERR_INVALID_ARG;
-  if ((long long)B * H * W * C > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
-  if ((long long)H * W * C >= (1LL << 29)) return PDR_ERR_INVALID_ARG;  // 32-bit frame offsets
+  const long long hw = (long long)H * W;   // each factor below 2^31: no overflow
+  if (hw >= (1LL << 29) || hw * C >= (1LL << 29)) return PDR_ERR_INVALID_ARG;  // 32-bit frame offsets
+  if ((long long)B * (hw * C) > 0x7fffffffLL) return PDR_ERR_INVALID_ARG;
   return (long long)loss_workspace_bytes(B, H, W, C);
 }
 

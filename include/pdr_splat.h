@@ -275,7 +275,8 @@ int pdr_splat_backward_algo(const float *params, const void *grad_image, int gra
  * prediction by concatenation).  out [B][H][W][Cp + C] receives, per pixel,
  * the Cp channels of pixel [B][H][W][Cp] followed by the C rendered
  * channels, written by the forward raster itself (no separate copy or
- * concat pass).  Cp >= 0; pixel may be NULL only when Cp = 0.  Same
+ * concat pass).  0 <= Cp and Cp + C <= 65536 (PDR_ERR_INVALID_ARG
+ * otherwise); pixel may be NULL only when Cp = 0.  Same
  * workspace, errors and overflow protocol as pdr_splat_forward. */
 int pdr_splat_forward_concat(const float *params, const float *pixel, int Cp, float *out, int B,
                              int N, int H, int W, int C, float radius, void *workspace,

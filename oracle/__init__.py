@@ -52,8 +52,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        # PDR_ORACLE_LIB: a separately built copy of oracle.c (the sanitizer
+        # test loads one built with ASan and UBSan)
+        path = os.environ.get("PDR_ORACLE_LIB")
+        if not path:
+            path = build(force=False)
+        lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int)
         lp = ctypes.POINTER(ctypes.c_longlong)
