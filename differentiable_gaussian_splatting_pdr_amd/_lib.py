@@ -23,6 +23,7 @@ PDR_ERR_STALE = -5
 EXPORTED = (
     "pdr_splat_tile_size",
     "pdr_splat_bin_variant",
+    "pdr_splat_backward_splits",
     "pdr_splat_count_support",
     "pdr_splat_workspace_bytes",
     "pdr_splat_forward",
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.pdr_splat_tile_size.restype = i
         L.pdr_splat_bin_variant.argtypes = [i, i, i, i]
         L.pdr_splat_bin_variant.restype = i
+        L.pdr_splat_backward_splits.argtypes = [i, i, i, i]
+        L.pdr_splat_backward_splits.restype = i
         L.pdr_splat_count_support.argtypes = [vp, i, i, i, i, i, f, vp, vp, sz, vp]
         L.pdr_splat_count_support.restype = i
         L.pdr_splat_workspace_bytes.argtypes = [i, i, i, i, i, ll]
@@ -161,6 +164,10 @@ def pdr_splat_count_support(params, B, N, H, W, C, radius, count, workspace, wor
 def pdr_splat_bin_variant(B, N, H, W) -> int:
     """Bit set of PDR_BIN_* for the binning a problem of this size takes."""
     return _raise(lib().pdr_splat_bin_variant(B, N, H, W), "pdr_splat_bin_variant")
+
+
+def pdr_splat_backward_splits(B, N, H, W) -> int:
+    return _raise(lib().pdr_splat_backward_splits(B, N, H, W), "pdr_splat_backward_splits")
 
 
 def pdr_splat_workspace_bytes(B, N, H, W, C, max_pairs) -> int:

@@ -216,6 +216,12 @@ int pdr_splat_bin_variant(int B, int N, int H, int W) {
   return rc != PDR_OK ? rc : bin_variant(B, N, H, W);
 }
 
+int pdr_splat_backward_splits(int B, int N, int H, int W) {
+  Dims d;
+  const int rc = validate_sizes(B, N, H, W, 1, &d);
+  return rc != PDR_OK ? rc : backward_splits(d.BT);
+}
+
 long long pdr_splat_workspace_bytes(int B, int N, int H, int W, int C, long long max_pairs) {
   Dims d;
   int rc = validate_sizes(B, N, H, W, C, &d);

@@ -472,6 +472,41 @@ __device__ __forceinline__ bool ordered_tile(int bid, int nT, int frames, const 
   return true;
 }
 
+// A grid whose items are each split S ways: block bid takes part
+// (bid >> 3) % S of the item that block (bid & 7) + 8 ((bid >> 3) / S) of
+// the unsplit grid would take, so an item's parts run consecutively on one
+// XCD.  Returns that unsplit block index.
+__device__ __forceinline__ int split_block(int bid, int S, int *part) {
+  const int k = bid >> 3;
+  *part = k % S;
+  return (bid & 7) | ((k / S) << 3);
+}
+
+// Workgroups per tile in the backward raster: one where the tiles fill the
+// chip several times over (at 8192 tiles and more, i.e. 8 per SIMD); for
+// batches of fewer tiles each tile's list is shared by 2, 4 or 8
+// workgroups, so that enough waves are resident to hide the raster's
+// latencies.  Measured on MI355X, backward raster: 160 frames of 64x64
+// (2560 tiles) 85 -> 48 us with 4, one 64x64 frame 28 -> 9 us with 8;
+// from 24576 tiles up one workgroup per tile is as fast or faster.
+#ifndef PDR_BWD_SPLITS
+#define PDR_BWD_SPLITS 0   // 0: by the number of tiles
+#endif
+inline int backward_splits(long long tiles) {
+  if (PDR_BWD_SPLITS > 0) return PDR_BWD_SPLITS;
+  return tiles >= 8192 ? 1 : (tiles >= 4096 ? 2 : (tiles >= 2048 ? 4 : 8));
+}
+
+// Waves per tile in the forward raster (the list shared as in the
+// backward, the shares' sums added in LDS): the same rule, at most 4.
+#ifndef PDR_FWD_SPLITS
+#define PDR_FWD_SPLITS 0   // 0: by the number of tiles
+#endif
+inline int forward_splits(long long tiles) {
+  if (PDR_FWD_SPLITS > 0) return PDR_FWD_SPLITS;
+  return tiles >= 8192 ? 1 : (tiles >= 4096 ? 2 : 4);
+}
+
 inline long long xcd_grid(int items, int frames) {
   return 8LL * (((long long)items * frames + 7) / 8);
 }

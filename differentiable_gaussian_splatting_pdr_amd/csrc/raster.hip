@@ -252,14 +252,28 @@ __device__ __forceinline__ float load_image(const void *base, size_t idx, int fm
   return (float)static_cast<const __bf16 *>(base)[idx];
 }
 
-template <int CP, int UW, int UX, int UY>
-__global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
+// Orders one wave's LDS accesses across its lanes (a wave's LDS operations
+// execute in order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// FS > 1 (one-wave tile layouts only): FS waves per tile, each walking a
+// contiguous share of the tile's list with its own staging area and no
+// workgroup barrier, their per-pixel sums added in wave order at the end
+// (deterministic).  For batches of few tiles, where one wave per tile
+// leaves the SIMDs short of resident waves.
+template <int CP, int UW, int UX, int UY, int FS = 1>
+__global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads * FS)) void k_forward(
     const GRec *__restrict__ recs, const ThinRec *__restrict__ thin,
     const float *__restrict__ params, const int *__restrict__ tile_off,
     const int *__restrict__ list, int B, int N, int H, int W, int C, int c0, int cc, float thr,
     int nTx, int nT, void *__restrict__ image, ImgView iv,
     const WsHeader *hdr, const int *__restrict__ order) {
   using WL = WaveLayout<UW, UX, UY>;
+  static_assert(FS == 1 || WL::kWaves == 1, "list shares need a one-wave tile layout");
   constexpr int UH = WL::kUH;
   int f, t;
   // Lists that overflowed are incomplete, and so is the tile order: every
@@ -268,11 +282,16 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
   if ((order && !ovf) ? !ordered_tile(blockIdx.x, nT, B, order, &f, &t)
                       : !xcd_frame_item(blockIdx.x, nT, B, &f, &t))
     return;
-  __shared__ Entry<CP> s[WL::kBatch];
-  __shared__ ThinX sx[WL::kBatch];
+  __shared__ Entry<CP> s_all[FS][WL::kBatch];
+  __shared__ ThinX sx_all[FS][WL::kBatch];
   __shared__ int scnt[2 * WL::kWaves];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
+  // region wave (tile layouts of several waves) and list share (FS > 1)
+  const int wave = FS > 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int part = FS > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) : 0;
+  const int stid = FS > 1 ? lane : tid;   // thread index within the staging group
+  Entry<CP> *s = s_all[part];
+  ThinX *sx = sx_all[part];
   const int tx0 = (t % nTx) * kTileW, ty0 = (t / nTx) * kTileH;
   const int rx0 = tx0, ry0 = ty0 + wave * WL::kRH;
   const int mshift = wave * WL::kUnitsPerWave;
@@ -294,12 +313,17 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
     beg = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t]);
     end = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t + 1]);
   }
+  if constexpr (FS > 1) {
+    const int share = (end - beg + FS - 1) / FS;
+    beg = min(end, beg + part * share);
+    end = min(end, beg + share);
+  }
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
-    __syncthreads();
+    if constexpr (FS > 1) wave_lds_sync(); else __syncthreads();
     const int np = stage_batch<CP, UW, WL::kWaves, true>(s, sx, scnt, recs, thin, params, list, s0, cnt,
-                                                   gbase, P, c0, cc, tid, tx0, ty0, thr);
-    __syncthreads();
+                                                   gbase, P, c0, cc, stid, tx0, ty0, thr);
+    if constexpr (FS > 1) wave_lds_sync(); else __syncthreads();
     // the entry loops run on scalar counts; each entry is read whole (its
     // unit mask is all but never empty for a listed Gaussian).  THIN: the
     // compensated evaluation of the batch's thin entries, after the others.
@@ -335,6 +359,30 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_forward(
     };
     run(IC<0>{}, 0, np);
     run(IC<1>{}, np, __builtin_amdgcn_readfirstlane(cnt));
+  }
+  if constexpr (FS > 1) {   // the shares' sums, added in wave order by wave 0
+    constexpr int V = UY * UX * CP;
+    __shared__ float red[(FS - 1) * V * kWave];
+    if (part > 0) {
+#pragma unroll
+      for (int j = 0; j < UY; ++j)
+#pragma unroll
+        for (int i = 0; i < UX; ++i)
+#pragma unroll
+          for (int c = 0; c < CP; ++c)
+            red[((part - 1) * V + (j * UX + i) * CP + c) * kWave + lane] = acc[j][i][c];
+    }
+    __syncthreads();
+    if (part > 0) return;
+    for (int w = 1; w < FS; ++w) {
+#pragma unroll
+      for (int j = 0; j < UY; ++j)
+#pragma unroll
+        for (int i = 0; i < UX; ++i)
+#pragma unroll
+          for (int c = 0; c < CP; ++c)
+            acc[j][i][c] += red[((w - 1) * V + (j * UX + i) * CP + c) * kWave + lane];
+    }
   }
 #pragma unroll
   for (int j = 0; j < UY; ++j) {
@@ -500,24 +548,30 @@ struct Pow2Up {
   static constexpr int value = K <= 8 ? 8 : (K <= 16 ? 16 : 32);
 };
 
-template <int CP, int UW, int UX, int UY>
+template <int CP, int UW, int UX, int UY, bool SPLIT = false>
 __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward(
     const GRec *__restrict__ recs, const ThinRec *__restrict__ thin,
     const float *__restrict__ params, const void *__restrict__ gimg,
     const int *__restrict__ tile_off,
     const int *__restrict__ list, int B, int N, int H, int W, int C, int c0, int cc, float thr,
     int nTx, int nT, float *__restrict__ sums, ImgView iv, WsHeader *hdr,
-    const int *__restrict__ order) {
+    const int *__restrict__ order, int splits) {
   using WL = WaveLayout<UW, UX, UY>;
   constexpr int UH = WL::kUH;
   constexpr int K = CP + 5;
   constexpr int KP = Pow2Up<K>::value;
-  int f, t;
+  int f, t, part = 0;
+  // SPLIT: a tile's list is walked by `splits` workgroups, each taking a
+  // contiguous share of its entries (every entry's sums leave through
+  // atomics, so the shares need no combining); a compile-time variant, so
+  // that the one-workgroup kernel carries none of it
+  int bid = (int)blockIdx.x;
+  if constexpr (SPLIT) bid = split_block(blockIdx.x, splits, &part);
   if (hdr->status & (kStatusOverflow | kStatusStale)) {
     // Binning that overflowed, or lists that are not this call's: no lists
     // to walk.  The finalisation sets dL/dparams to NaN; the pixel branch's
     // gradient slice (concat) is set to NaN here, tiles in launch order.
-    if (iv.xout && xcd_frame_item(blockIdx.x, nT, B, &f, &t)) {
+    if (iv.xout && (!SPLIT || part == 0) && xcd_frame_item(bid, nT, B, &f, &t)) {
       const int px0 = (t % nTx) * kTileW, py0 = (t / nTx) * kTileH;
       for (int k = threadIdx.x; k < kTileW * kTileH; k += WL::kThreads) {
         const int px = px0 + k % kTileW, py = py0 + k / kTileW;
@@ -528,8 +582,7 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
     }
     return;
   }
-  if (order ? !ordered_tile(blockIdx.x, nT, B, order, &f, &t)
-            : !xcd_frame_item(blockIdx.x, nT, B, &f, &t))
+  if (order ? !ordered_tile(bid, nT, B, order, &f, &t) : !xcd_frame_item(bid, nT, B, &f, &t))
     return;
   __shared__ Entry<CP> s[WL::kBatch];
   __shared__ ThinX sx[WL::kBatch];
@@ -556,7 +609,7 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
       const size_t g = pix * (size_t)iv.ldo + iv.ooff + c0;
 #pragma unroll
       for (int c = 0; c < CP; ++c) G[j][i][c] = (in && c < cc) ? load_image(gimg, g + c, iv.fmt) : 0.f;
-      if (iv.xout && in) {   // concat fusion: the pixel branch's gradient slice (fp32 only)
+      if (iv.xout && in && (!SPLIT || part == 0)) {   // concat fusion: the pixel branch's gradient slice (fp32 only)
         const float *gb = static_cast<const float *>(gimg) + pix * (size_t)iv.ldo;
         float *xo = iv.xout + pix * (size_t)iv.Cp;
         for (int c = 0; c < iv.Cp; ++c) xo[c] = gb[c];
@@ -602,8 +655,13 @@ __global__ __launch_bounds__((WaveLayout<UW, UX, UY>::kThreads)) void k_backward
     else if (vidx < K) slot = vidx - CP;
   }
 
-  const int beg = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t]);
-  const int end = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t + 1]);
+  int beg = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t]);
+  int end = __builtin_amdgcn_readfirstlane(tile_off[(size_t)f * nT + t + 1]);
+  if constexpr (SPLIT) {
+    const int share = (end - beg + splits - 1) / splits;
+    beg = min(end, beg + part * share);
+    end = min(end, beg + share);
+  }
   for (int s0 = beg; s0 < end; s0 += WL::kBatch) {
     const int cnt = min(WL::kBatch, end - s0);
     __syncthreads();
@@ -811,26 +869,39 @@ struct RasterArgs {
   const int *order;
 };
 
-template <int CP, int UW, int UX, int UY>
-void fwd_cp(const RasterArgs &a, hipStream_t st) {
+template <int CP, int UW, int UX, int UY, int FS>
+void fwd_launch(const RasterArgs &a, hipStream_t st) {
   using WL = WaveLayout<UW, UX, UY>;
   dim3 grid((unsigned)xcd_grid(a.nT, a.B));
   PDR_TIMED(PDR_K_FORWARD_RASTER, st,
-            hipLaunchKernelGGL((k_forward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
-                               a.recs, a.thin, a.params, a.tile_off, a.list, a.B, a.N, a.H, a.W,
-                               a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr, a.order));
+            hipLaunchKernelGGL((k_forward<CP, UW, UX, UY, FS>), grid, dim3(WL::kThreads * FS), 0,
+                               st, a.recs, a.thin, a.params, a.tile_off, a.list, a.B, a.N, a.H,
+                               a.W, a.C, a.c0, a.cc, a.thr, a.nTx, a.nT, a.out, a.iv, a.hdr,
+                               a.order));
+}
+
+template <int CP, int UW, int UX, int UY>
+void fwd_cp(const RasterArgs &a, hipStream_t st) {
+  if constexpr (CP <= 4 && WaveLayout<UW, UX, UY>::kWaves == 1) {
+    const int fs = forward_splits((long long)a.nT * a.B);
+    if (fs >= 4) return fwd_launch<CP, UW, UX, UY, 4>(a, st);
+    if (fs == 2) return fwd_launch<CP, UW, UX, UY, 2>(a, st);
+  }
+  fwd_launch<CP, UW, UX, UY, 1>(a, st);
 }
 
 template <int CP, int UW, int UX, int UY>
 void bwd_cp(const RasterArgs &a, hipStream_t st) {
   using WL = WaveLayout<UW, UX, UY>;
-  dim3 grid((unsigned)xcd_grid(a.nT, a.B));
+  const int splits = backward_splits((long long)a.nT * a.B);
+  dim3 grid((unsigned)(xcd_grid(a.nT, a.B) * splits));
+  auto kern = splits > 1 ? k_backward<CP, UW, UX, UY, true> : k_backward<CP, UW, UX, UY, false>;
   PDR_TIMED(PDR_K_BACKWARD_RASTER, st,
-            hipLaunchKernelGGL((k_backward<CP, UW, UX, UY>), grid, dim3(WL::kThreads), 0, st,
+            hipLaunchKernelGGL(kern, grid, dim3(WL::kThreads), 0, st,
                                a.recs, a.thin, a.params, a.gimg, a.tile_off, a.list, a.B, a.N,
                                a.H, a.W, a.C, a.c0, a.cc, a.thr, a.nTx, a.nT,
                                static_cast<float *>(a.out),
-                               a.iv, const_cast<WsHeader *>(a.hdr), a.order));
+                               a.iv, const_cast<WsHeader *>(a.hdr), a.order, splits));
 }
 
 // Unit shape and units per wave (compile-time tuning knob): 8x8 quads,

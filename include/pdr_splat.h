@@ -76,6 +76,14 @@ int pdr_splat_tile_size(void);
 enum { PDR_BIN_MEMBERS = 1, PDR_BIN_COLUMNS = 2, PDR_BIN_TWO_LEVEL = 4 };
 int pdr_splat_bin_variant(int B, int N, int H, int W);
 
+/* Inspection: how many workgroups share each tile's list in the tile
+ * backward raster (host only, no device call): 1 from 8192 tiles in the
+ * batch (B * ceil(W/16) * ceil(H/16)), 2 from 4096, 4 from 2048, else 8.
+ * Each takes a contiguous share of the tile's entries; the results are
+ * the same up to the order of the atomic additions.  Negative pdr_status
+ * on invalid sizes. */
+int pdr_splat_backward_splits(int B, int N, int H, int W);
+
 /* Bytes of workspace for a problem and a (tile, Gaussian) pair capacity.
  * Returns a negative pdr_status on invalid sizes.  The fixed part covers a
  * 256-byte header, 72 bytes per Gaussian (its raster record, the

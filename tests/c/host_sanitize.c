@@ -158,6 +158,8 @@ int main(void) {
                         }
                         int v = pdr_splat_bin_variant(B, N, H, W);
                         EXPECT((v >= 0 && v <= 7) || v == PDR_ERR_INVALID_ARG);
+                        int sp = pdr_splat_backward_splits(B, N, H, W);
+                        EXPECT(sp == 1 || sp == 2 || sp == 4 || sp == 8 || sp == PDR_ERR_INVALID_ARG);
                     }
     }
 

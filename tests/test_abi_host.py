@@ -259,3 +259,18 @@ else:
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 0, r.stdout + r.stderr
     assert "render raised" in r.stdout
+
+
+@pytest.mark.parametrize("B,H,W,S", [(1, 16, 16, 8), (2047, 16, 16, 8), (2048, 16, 16, 4),
+                                     (4095, 16, 16, 4), (4096, 16, 16, 2), (8191, 16, 16, 2),
+                                     (8192, 16, 16, 1), (1, 1024, 2048, 1), (2, 1000, 1000, 2),
+                                     (40, 128, 128, 4), (72, 128, 128, 2), (130, 128, 128, 1)])
+def test_backward_splits_rule(B, H, W, S):
+    """Workgroups per tile of the tile backward, by the batch's tile count."""
+    assert _lib.pdr_splat_backward_splits(B, 64, H, W) == S
+
+
+def test_backward_splits_validates():
+    for args in ((0, 64, 16, 16), (1, 0, 16, 16), (1, 64, 0, 16), (1, 64, 16, 40000)):
+        with pytest.raises(_lib.PdrError):
+            _lib.pdr_splat_backward_splits(*args)

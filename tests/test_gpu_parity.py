@@ -450,3 +450,19 @@ def test_many_small_frames_bin_linearly(orc):
         times[B] = e0.elapsed_time(e1) / 5
     print("binning ms", times)
     assert times[20000] < 8.0 * times[5000]
+
+
+@pytest.mark.parametrize("B,H,W,S", [(2, 64, 64, 8), (40, 128, 128, 4), (72, 128, 128, 2),
+                                     (130, 128, 128, 1)])
+def test_backward_split_tiles(orc, B, H, W, S):
+    """The tile backward with each tile's list shared by S workgroups (the
+    count the batch's size selects, asserted first) against the oracle,
+    every frame, with and without reusing the forward's binning."""
+    from differentiable_gaussian_splatting_pdr_amd import _lib
+    N, C = 300, 3
+    assert _lib.pdr_splat_backward_splits(B, N, H, W) == S
+    p, g = workloads.make_custom(B, N, H, W, C, seed=100 + S, s_range=(0.4, 8.0), mean_margin=4.0)
+    gr, gsl, gmag = orc.grad(p, g, H, W)
+    for reuse in (True, False):
+        out = gpu_forward_backward(p, g, H, W, reuse=reuse, algo="tile")
+        check_grad(out["grad"], gr, gmag, gsl, "split %d reuse %d" % (S, reuse))
