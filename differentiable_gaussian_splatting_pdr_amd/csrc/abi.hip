@@ -78,11 +78,12 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PDR_OK : PDR_ERR_HIP; }
 
 // Which backward PDR_BWD_AUTO takes where both apply: the span walk for
 // small problems, where its single launch (no zeroing, no finalisation)
-// wins -- measured on MI355X 0.60x the tile backward's time at 1 x 64x64,
-// N = 256, a tie at 160 x 1024 Gaussians and 1.26-1.72x from 32 x 4096
-// Gaussians up -- and the tile raster otherwise.
+// wins, and the tile raster otherwise.  Measured on MI355X (backward alone,
+// the tile raster sharing each tile's list among workgroups for such small
+// batches): span/tile 1.02 at 256 and 1024 Gaussians, 0.79-0.96 from 4096
+// to 16384 (1 to 3 channels), 1.22-1.25 at 32768 and 1.75 at 160 x 1024.
 #ifndef PDR_AUTO_SPAN_MAX_GAUSSIANS
-#define PDR_AUTO_SPAN_MAX_GAUSSIANS 32768
+#define PDR_AUTO_SPAN_MAX_GAUSSIANS 16384
 #endif
 bool auto_span(int B, int N) {
   return (long long)B * N <= PDR_AUTO_SPAN_MAX_GAUSSIANS;

@@ -265,7 +265,7 @@ int pdr_splat_backward_fmt(const float *params, const void *grad_image, int grad
  * zeroing, no finalisation pass); it needs only the per-Gaussian records, so
  * without reuse it runs no tile binning.  C <= 16 and H*W*C < 2^29.  PDR_BWD_AUTO: the
  * library's default (what pdr_splat_backward uses): the span walk where it
- * applies and B*N <= 32768 (small, launch-bound problems), else the tile
+ * applies and B*N <= 16384 (small, launch-bound problems), else the tile
  * raster.  Both compute the same sums within the same tolerance. */
 typedef enum { PDR_BWD_AUTO = 0, PDR_BWD_TILE = 1, PDR_BWD_SPAN = 2 } pdr_backward_algo;
 

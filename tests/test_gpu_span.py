@@ -164,7 +164,7 @@ def test_span_rebin_leaves_no_reusable_binning(orc):
 
 
 def test_auto_choice(orc):
-    # the library default takes the span walk for small problems (B*N <= 32768)
+    # the library default takes the span walk for small problems (B*N <= 16384)
     # and the tile raster beyond; the span walk is deterministic (no atomics),
     # so the small default result equals the explicit span result bit for bit
     from differentiable_gaussian_splatting_pdr_amd import _lib
