@@ -229,3 +229,79 @@ def test_status_async_rejects_bad_pointers():
         with pytest.raises(_lib.PdrError) as ei:
             _lib.pdr_splat_status_async(args[0], args[1], st)
         assert ei.value.status == rc
+
+
+def test_evicted_workspace_still_reports_its_overflow(monkeypatch):
+    """A size evicted (least recently used) while its last call's report is
+    in flight: the report is still read, and flush() raises its overflow."""
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import _lib, splat
+    p, big, _ = _big_small()
+    H = W = 128
+    r = splat.Renderer(headroom=1.0, max_entries=2)
+    small_t, big_t = torch.from_numpy(p).cuda(), torch.from_numpy(big).cuda()
+    splat.render(small_t, H, W, 3.0, renderer=r)              # size A made
+    splat.render(big_t, H, W, 3.0, renderer=r)                # A overflows, unchecked
+    for B in (3, 4):                                          # sizes B and C: A evicted
+        q, _ = workloads.make_custom(B, 64, 48, 48, 1, seed=B)
+        splat.render(torch.from_numpy(q).cuda(), 48, 48, 3.0, renderer=r)
+    assert len(r._entries) == 2
+    with pytest.raises(_lib.PdrError) as ei:
+        r.flush()
+    assert ei.value.status == _lib.PDR_ERR_OVERFLOW
+    r.flush()
+
+
+def test_bounded_reports_in_flight(monkeypatch):
+    """With at most two reports in flight, a loop of renders waits for the
+    oldest instead of growing the queue, and stays exact."""
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import splat
+    B, N, H, W, C = 2, 200, 64, 80, 3
+    p, _ = workloads.make_custom(B, N, H, W, C, seed=51)
+    pt = torch.from_numpy(p).cuda()
+    r = splat.Renderer(max_pending=2)
+    cnt = _CountChecks(monkeypatch)
+    imgs = [splat.render(pt, H, W, 3.0, renderer=r) for _ in range(8)]
+    e = next(iter(r._entries.values()))
+    assert len(e.pending) <= 2
+    r.flush()
+    cnt.stop()
+    assert cnt.n == 1
+    ref, _ = splat.forward(pt, H, W, 3.0)
+    for img in imgs:
+        assert torch.equal(img, ref)
+
+
+def test_renders_from_two_threads_on_their_own_streams():
+    """Two host threads, each with its own stream: one workspace per
+    stream, results equal to the one-shot path."""
+    import threading
+    import torch
+    from differentiable_gaussian_splatting_pdr_amd import splat
+    r = splat.Renderer()
+    out, errs = {}, []
+    sets = {k: workloads.make_custom(2, 150, 40, 56, 2, seed=70 + k)[0] for k in range(2)}
+
+    def work(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                pt = torch.from_numpy(sets[k]).cuda()
+                for _ in range(4):
+                    img = splat.render(pt, 40, 56, 3.0, renderer=r)
+                s.synchronize()
+                out[k] = img
+        except Exception as e:   # reported below
+            errs.append(e)
+    th = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errs, errs
+    r.flush()
+    assert len(r._entries) == 2   # (device, stream, sizes) keys differ by stream
+    for k in range(2):
+        ref, _ = splat.forward(torch.from_numpy(sets[k]).cuda(), 40, 56, 3.0)
+        assert torch.equal(out[k], ref)
